@@ -1,0 +1,180 @@
+/*
+ * qr.h - C ABI of the QuaRot 4-bit linear-layer inference hot path on AMD
+ * MI355X (gfx950).
+ *
+ * The method (QuaRot; abstract of the ISTA Research Explorer record and the
+ * "Summary" / "Key points" of the Elamur Research summary): rotate the input
+ * of a linear layer Y = X W by an orthogonal matrix R online, quantize the
+ * rotated activations to 4 bits with round-to-nearest, multiply them in
+ * integers against weights that were rotated by R^T and quantized offline,
+ * and dequantize the output; the KV cache is stored in 4 bits after a
+ * head-wise Hadamard rotation.  The identity that makes this exact before
+ * quantization is Y = XW = (XR)(R^T W) (DuQuant page, Knowl 1).
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" are HIP device (or managed) pointers; every
+ *    call is asynchronous on `stream` (a hipStream_t passed as void*, NULL =
+ *    the null stream) and never synchronises.
+ *  - The caller owns every buffer.  The library keeps no pointer after
+ *    return, allocates nothing, holds no mutable global state and may be
+ *    called concurrently from several host threads.
+ *  - Arguments are validated on the host before anything is launched.  On a
+ *    bad argument the call returns a non-zero qr_status, launches nothing and
+ *    writes nothing.  QR_EDEVICE reports a failed launch; faults inside a
+ *    kernel surface at the caller's next synchronisation.
+ *  - Inputs must be finite; non-finite input gives unspecified codes.
+ *  - fp16 data is IEEE binary16 stored as 16-bit words.
+ *  - Packed 4-bit codes: two per byte, the element with the even index in
+ *    the low nibble.  Symmetric codes are two's complement in [-8, 7];
+ *    KV codes are unsigned in [0, 15].
+ */
+#ifndef QR_H
+#define QR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QR_OK = 0,
+  QR_EINVAL = 1,   /* null pointer, bad enum value, negative size        */
+  QR_ESHAPE = 2,   /* sizes the operation does not support               */
+  QR_EALIGN = 3,   /* pointer or leading dimension not aligned as needed */
+  QR_EDEVICE = 4   /* the HIP runtime reported an error at launch        */
+} qr_status;
+
+/*
+ * An orthogonal rotation R of row width n, applied as y = x R.
+ *
+ *   dense_m == 1:  R = D . H_n / sqrt(n)                   (had_n == n)
+ *   dense_m  > 1:  R = D . ((H_p / sqrt(p)) kron O)         (p = had_n)
+ *
+ * H_p is the Sylvester Hadamard matrix in natural order (H_1 = [1],
+ * H_2k = [[H_k, H_k], [H_k, -H_k]]), normalised by 1/sqrt(p) as the DuQuant
+ * page (Knowl 12) states for its fixed Hadamard rotations.  D = diag(signs)
+ * is the random +-1 diagonal of the randomized Hadamard transform (QuaRot
+ * press article; QuaRot summary, "Summary"), applied to the input before the
+ * transform.  O is a dense dense_m x dense_m orthogonal factor (random
+ * orthogonal multiplication: QuIP summary, abstract; two-factor Kronecker
+ * construction: the QuIP# quote on the same page) used where n is not a
+ * power of two, e.g. n = 11008 = 64 * 172.  In the Kronecker product the
+ * dense index is the fastest: element k = i * dense_m + a.
+ *
+ * Fields: n = had_n * dense_m, n even, 2 <= n <= 16384, had_n a power of two
+ * in [1, 8192], dense_m in [1, 256].  `dense` (device, fp32, row-major
+ * [dense_m][dense_m]) must be NULL iff dense_m == 1; the library does not
+ * check that it is orthogonal.  `signs` (device, int8 [n], each +1 or -1)
+ * may be NULL for D = I.
+ */
+typedef struct {
+  int64_t n;
+  int64_t had_n;
+  int64_t dense_m;
+  const float *dense;
+  const int8_t *signs;
+} qr_rotation;
+
+/*
+ * Online rotation + symmetric 4-bit round-to-nearest quantization + packing
+ * of `rows` activation rows (QuaRot summary, "Key points": activations
+ * quantized on the fly with RTN; group size 128 as the group-wise option).
+ *
+ *   y     = x[r, :] R                      (fp32 arithmetic on fp16 input)
+ *   s     = max |y| / 7 over the row (group == 0) or over each contiguous
+ *           block of `group` elements of y
+ *   q     = clamp(rint(y / s), -8, 7)      (round half to even)
+ *   s = 0 and q = 0 for an all-zero row or group.
+ *
+ * x_f16   device, fp16, row r at x_f16 + r * ld_x (elements); ld_x >= n,
+ *         ld_x a multiple of 8, x_f16 16-byte aligned.
+ * rows    >= 0 (0 is a no-op).
+ * group   0 (per row) or a power of two >= 32 that divides n.
+ * codes   device, [rows][n/2] bytes, 16-byte aligned.
+ * scales  device, fp32 [rows] (group 0) or [rows][n/group].
+ *
+ * The same call prepares weights offline: since (R^T W)^T = W^T R, rotating
+ * and quantizing the rows of W^T ([N][K]) gives per-output-channel (or
+ * group-wise along K) weight codes and scales in the layout qr_int4_gemm
+ * takes.
+ */
+qr_status qr_rotate_quant(const void *x_f16, int64_t rows, int64_t ld_x,
+                          const qr_rotation *rot, int64_t group,
+                          uint8_t *codes, float *scales, void *stream);
+
+/*
+ * 4-bit integer GEMM with a dequantizing fp16 epilogue (QuaRot abstract: all
+ * matrix multiplications performed in 4 bits).
+ *
+ *   acc[t, n]  = sum_k qa[t, k] * qw[n, k]            exact integer sum
+ *   group 0:   y[t, n] = fp16(acc[t, n] * a_scales[t] * w_scales[n])
+ *   group g:   y[t, n] = fp16(sum_j acc_j[t, n] * a_scales[t, j] * w_scales[n, j])
+ *              acc_j summing k in [j g, (j+1) g)
+ * The scale products and the sum over groups are formed in fp32; the
+ * conversion to fp16 rounds to nearest even.
+ *
+ * a_codes   device, [M][K/2] packed two's-complement codes (16-byte aligned)
+ * a_scales  device, fp32 [M] or [M][K/group]
+ * w_codes   device, [N][K/2] packed codes, one row per output channel
+ * w_scales  device, fp32 [N] or [N][K/group]
+ * M, N >= 0; K > 0 and a multiple of 128; group 0 or a multiple of 128 that
+ * divides K.
+ * y_f16     device, fp16 [M][ld_y], ld_y >= N, ld_y even, 4-byte aligned.
+ *
+ * M <= 64 runs the memory-bound decode kernel (weights streamed once); larger
+ * M runs the MFMA-bound prefill kernel.  Both give identical integer sums.
+ */
+qr_status qr_int4_gemm(const uint8_t *a_codes, const float *a_scales,
+                       const uint8_t *w_codes, const float *w_scales,
+                       int64_t M, int64_t N, int64_t K, int64_t group,
+                       void *y_f16, int64_t ld_y, void *stream);
+
+/*
+ * Head-wise rotated asymmetric 4-bit KV-cache quantization (QuaRot abstract:
+ * the KV cache in 4 bits; DuQuant page, Knowl 12: fixed Hadamard rotation
+ * +-1/sqrt(2^n) with per-token / per-head asymmetric quantization and the
+ * step (gamma max - beta min)/(2^b - 1), here gamma = beta = 1, b = 4).
+ *
+ * For every token t and head h, with v = kv[t, h, :]:
+ *   y    = (v * signs) H_D / sqrt(D)        (signs optional; D = head_dim)
+ *   lo   = min(min y, 0),  hi = max(max y, 0),  step = (hi - lo) / 15
+ *   z    = rint(-lo / step)
+ *   q    = clamp(rint(y / step) + z, 0, 15)
+ *   step = 0, z = 0, q = 0 when hi == lo.
+ * Dequantization is (q - z) * step in the rotated domain.
+ *
+ * kv_f16  device fp16; element (t, h, d) at kv_f16 + t * ld_kv + h * head_dim + d.
+ *         ld_kv >= H * head_dim, multiple of 8; 16-byte aligned.  This lets
+ *         the K or V slice of a fused QKV output be quantized in place.
+ * T, H    >= 0; head_dim == 128.
+ * signs   device int8 [head_dim] of +-1, or NULL.
+ * codes   device [T][H][head_dim/2] unsigned packed codes (16-byte aligned)
+ * scales  device fp32 [T][H] (the step)
+ * zeros   device uint8 [T][H] (the zero point z)
+ */
+qr_status qr_kv_quant(const void *kv_f16, int64_t T, int64_t H, int64_t head_dim,
+                      int64_t ld_kv, const int8_t *signs,
+                      uint8_t *codes, float *scales, uint8_t *zeros, void *stream);
+
+/*
+ * Test and diagnostic export: the exact integer sums of qr_int4_gemm without
+ * the epilogue, from the same kernels.  acc is int32 [M][N] (group 0) or
+ * [K/group][M][N] (one slice per group), contiguous.  Same argument rules as
+ * qr_int4_gemm.
+ */
+qr_status qr_int4_gemm_i32(const uint8_t *a_codes, const uint8_t *w_codes,
+                           int64_t M, int64_t N, int64_t K, int64_t group,
+                           int32_t *acc, void *stream);
+
+/* Static English text for a status code (never NULL). */
+const char *qr_status_str(qr_status s);
+
+/* Library version as 10000 * major + 100 * minor + patch. */
+int qr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QR_H */

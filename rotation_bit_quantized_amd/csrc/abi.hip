@@ -1,0 +1,121 @@
+// The exported C ABI (include/qr.h): argument validation on the host, then
+// dispatch to the kernels.  Nothing here allocates, synchronises or keeps
+// state; a rejected call launches nothing.
+#include "../../include/qr.h"
+#include "qr_launch.h"
+
+namespace {
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+qr_status from_hip(hipError_t e) { return e == hipSuccess ? QR_OK : QR_EDEVICE; }
+
+qr_status check_rotation(const qr_rotation *rot) {
+  if (rot == nullptr) return QR_EINVAL;
+  if (rot->n <= 0 || rot->had_n <= 0 || rot->dense_m <= 0) return QR_EINVAL;
+  if (!pow2(rot->had_n) || rot->had_n > 8192) return QR_ESHAPE;
+  if (rot->dense_m > 256) return QR_ESHAPE;
+  if (rot->n != rot->had_n * rot->dense_m) return QR_ESHAPE;
+  if (rot->n < 2 || rot->n > 16384 || (rot->n & 1)) return QR_ESHAPE;
+  if ((rot->dense == nullptr) != (rot->dense_m == 1)) return QR_EINVAL;
+  if (rot->dense != nullptr && !aligned(rot->dense, 4)) return QR_EALIGN;
+  return QR_OK;
+}
+
+qr_status check_gemm(const uint8_t *a, const uint8_t *w, int64_t M, int64_t N, int64_t K, int64_t group) {
+  if (M < 0 || N < 0 || K <= 0) return QR_EINVAL;
+  if (K % 128 != 0 || K > (int64_t)1 << 20) return QR_ESHAPE;
+  if (group != 0 && (group < 128 || group % 128 != 0 || K % group != 0)) return QR_ESHAPE;
+  if (M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30)) return QR_ESHAPE;
+  if (M == 0 || N == 0) return QR_OK;
+  if (a == nullptr || w == nullptr) return QR_EINVAL;
+  if (!aligned(a, 16) || !aligned(w, 16)) return QR_EALIGN;
+  return QR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qr_status_str(qr_status s) {
+  switch (s) {
+    case QR_OK: return "ok";
+    case QR_EINVAL: return "invalid argument (null pointer, negative size or bad value)";
+    case QR_ESHAPE: return "unsupported shape";
+    case QR_EALIGN: return "misaligned pointer or leading dimension";
+    case QR_EDEVICE: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+int qr_version(void) { return 100; }
+
+qr_status qr_rotate_quant(const void *x_f16, int64_t rows, int64_t ld_x, const qr_rotation *rot,
+                          int64_t group, uint8_t *codes, float *scales, void *stream) {
+  qr_status st = check_rotation(rot);
+  if (st != QR_OK) return st;
+  if (rows < 0) return QR_EINVAL;
+  if (group != 0 && (group < 32 || !pow2(group) || rot->n % group != 0)) return QR_ESHAPE;
+  if (ld_x < rot->n) return QR_ESHAPE;
+  if (ld_x % 8 != 0) return QR_EALIGN;
+  if (rows == 0) return QR_OK;
+  if (x_f16 == nullptr || codes == nullptr || scales == nullptr) return QR_EINVAL;
+  if (!aligned(x_f16, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return QR_EALIGN;
+  if (rot->signs != nullptr && !aligned(rot->signs, 1)) return QR_EALIGN;
+
+  qr::RotArgs r{(int)rot->n, (int)rot->had_n, (int)rot->dense_m, rot->dense, rot->signs};
+  hipStream_t s = (hipStream_t)stream;
+  if (qr::rq_pow2_supported(r, (int)group))
+    return from_hip(qr::launch_rq_pow2(x_f16, rows, ld_x, r, (int)group, codes, scales, s));
+  if (qr::rq_kron_supported(r, (int)group))
+    return from_hip(qr::launch_rq_kron(x_f16, rows, ld_x, r, (int)group, codes, scales, s));
+  return from_hip(qr::launch_rq_generic(x_f16, rows, ld_x, r, (int)group, codes, scales, s));
+}
+
+qr_status qr_int4_gemm(const uint8_t *a_codes, const float *a_scales, const uint8_t *w_codes,
+                       const float *w_scales, int64_t M, int64_t N, int64_t K, int64_t group, void *y_f16,
+                       int64_t ld_y, void *stream) {
+  qr_status st = check_gemm(a_codes, w_codes, M, N, K, group);
+  if (st != QR_OK) return st;
+  if (ld_y < N) return QR_ESHAPE;
+  if (M == 0 || N == 0) return QR_OK;
+  if (a_scales == nullptr || w_scales == nullptr || y_f16 == nullptr) return QR_EINVAL;
+  if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(y_f16, 2)) return QR_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (M <= 64)
+    return from_hip(qr::launch_gemm_decode(a_codes, a_scales, w_codes, w_scales, M, N, K, (int)group, y_f16,
+                                           ld_y, false, s));
+  return from_hip(qr::launch_gemm_prefill(a_codes, a_scales, w_codes, w_scales, M, N, K, (int)group, y_f16,
+                                          ld_y, false, s));
+}
+
+qr_status qr_int4_gemm_i32(const uint8_t *a_codes, const uint8_t *w_codes, int64_t M, int64_t N, int64_t K,
+                           int64_t group, int32_t *acc, void *stream) {
+  qr_status st = check_gemm(a_codes, w_codes, M, N, K, group);
+  if (st != QR_OK) return st;
+  if (M == 0 || N == 0) return QR_OK;
+  if (acc == nullptr) return QR_EINVAL;
+  if (!aligned(acc, 4)) return QR_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (M <= 64)
+    return from_hip(qr::launch_gemm_decode(a_codes, nullptr, w_codes, nullptr, M, N, K, (int)group, acc, N,
+                                           true, s));
+  return from_hip(qr::launch_gemm_prefill(a_codes, nullptr, w_codes, nullptr, M, N, K, (int)group, acc, N,
+                                          true, s));
+}
+
+qr_status qr_kv_quant(const void *kv_f16, int64_t T, int64_t H, int64_t head_dim, int64_t ld_kv,
+                      const int8_t *signs, uint8_t *codes, float *scales, uint8_t *zeros, void *stream) {
+  if (T < 0 || H < 0) return QR_EINVAL;
+  if (head_dim != 128) return QR_ESHAPE;
+  if (H > ((int64_t)1 << 20)) return QR_ESHAPE;
+  if (ld_kv < H * head_dim) return QR_ESHAPE;
+  if (ld_kv % 8 != 0) return QR_EALIGN;
+  if (T == 0 || H == 0) return QR_OK;
+  if (kv_f16 == nullptr || codes == nullptr || scales == nullptr || zeros == nullptr) return QR_EINVAL;
+  if (!aligned(kv_f16, 16) || !aligned(codes, 4) || !aligned(scales, 4)) return QR_EALIGN;
+  return from_hip(qr::launch_kv_quant(kv_f16, T, H, ld_kv, signs, codes, scales, zeros, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+// 4-bit integer GEMM for decode shapes (M <= 64 tokens): memory-bound, the
+// weight codes are streamed from HBM exactly once.
+//
+// Method: as the prefill kernel (QuaRot abstract: all matrix
+// multiplications in 4 bits; dequantizing epilogue per output channel or
+// per K-group of 128).  Decoding is the memory-bound phase where the 4-bit
+// weights cut the bytes moved (QuaRot summary, "Key points": decode peak
+// memory; QuaRot press article: decoding is usually memory-bound).
+//
+// One workgroup (16 waves) owns 16 output channels and all M <= 64 tokens.
+// Wave w handles the K-units w, w + 16, ... (a unit is 64 codes per-channel,
+// or one 128-group); per unit it loads the 16 weight rows (8 bytes per lane)
+// and the 64 token rows (4 x 8 bytes per lane) straight into registers,
+// widens them to 16*q int8 (see gemm_prefill.hip) and issues
+// v_mfma_i32_16x16x64_i8 with A = weight rows, B = token rows, giving
+// C[channel][token].  The 16 per-wave partials are reduced through LDS in
+// int32 (per-channel, exact) or fp32 (group-wise, after scaling).
+#include "qr_common.h"
+#include "qr_launch.h"
+
+namespace qr {
+namespace {
+
+constexpr int kWaves = 16;
+constexpr int kNT = 16;  // output channels per workgroup
+
+__device__ __forceinline__ v4i widen8(v2u w) {
+  v4i op;
+  op[0] = (int)((w[0] << 4) & 0xF0F0F0F0u);
+  op[1] = (int)(w[0] & 0xF0F0F0F0u);
+  op[2] = (int)((w[1] << 4) & 0xF0F0F0F0u);
+  op[3] = (int)(w[1] & 0xF0F0F0F0u);
+  return op;
+}
+
+template <bool GROUPED, bool OUT_I32>
+__global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
+    const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ W,
+    const float *__restrict__ sw, int M, int N, int K, int group, void *__restrict__ out, int64_t ld_y) {
+  // partial sums: [wave][frag 0..3][lane][4], int32 or fp32 bits
+  __shared__ int red[kWaves][4][64][4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n0 = blockIdx.x * kNT;
+  const int64_t kbytes = K / 2;
+  const int ksteps_per_unit = GROUPED ? group / 64 : 1;
+  const int units = K / 64 / ksteps_per_unit;
+  const int G = GROUPED ? K / group : 1;
+
+  const int wrow = n0 + (lane & 15);                 // weight row (output channel) of this lane
+  const int kofs = (lane >> 4) * 8;                  // byte offset of this lane's 16 codes in a 64-code step
+  const bool wvalid = wrow < N;
+  const uint8_t *wp = W + (int64_t)(wvalid ? wrow : 0) * kbytes + kofs;
+  const uint8_t *ap[4];
+  bool avalid[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int t = f * 16 + (lane & 15);
+    avalid[f] = t < M;
+    ap[f] = A + (int64_t)(avalid[f] ? t : 0) * kbytes + kofs;
+  }
+
+  v4i acc[4] = {v4i{}, v4i{}, v4i{}, v4i{}};
+  v4f facc[4] = {v4f{}, v4f{}, v4f{}, v4f{}};
+
+  for (int u = wave; u < units; u += kWaves) {
+    v4i uacc[4] = {v4i{}, v4i{}, v4i{}, v4i{}};
+    for (int s = 0; s < ksteps_per_unit; ++s) {
+      const int64_t off = (int64_t)(u * ksteps_per_unit + s) * 32;
+      v2u wv = wvalid ? __builtin_nontemporal_load((const v2u *)(wp + off)) : v2u{0u, 0u};
+      v2u av[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) av[f] = avalid[f] ? *(const v2u *)(ap[f] + off) : v2u{0u, 0u};
+      const v4i wop = widen8(wv);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        if (GROUPED)
+          uacc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, widen8(av[f]), uacc[f], 0, 0, 0);
+        else
+          acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, widen8(av[f]), acc[f], 0, 0, 0);
+      }
+    }
+    if constexpr (GROUPED) {
+      // this lane holds C[channel 4*(lane/16)+r][token f*16 + lane%16]
+      if constexpr (OUT_I32) {
+        int32_t *o = (int32_t *)out + (int64_t)u * M * N;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int t = f * 16 + (lane & 15);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int ch = n0 + 4 * (lane >> 4) + r;
+            if (t < M && ch < N) o[(int64_t)t * N + ch] = uacc[f][r] >> 8;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int t = f * 16 + (lane & 15);
+          const float sav = t < M ? sa[(int64_t)t * G + u] * (1.0f / 256.0f) : 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int ch = n0 + 4 * (lane >> 4) + r;
+            const float swv = ch < N ? sw[(int64_t)ch * G + u] : 0.f;
+            facc[f][r] = __builtin_fmaf((float)uacc[f][r], sav * swv, facc[f][r]);
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (GROUPED && OUT_I32) return;
+
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][f][lane][r] = GROUPED ? (int)f2u(facc[f][r]) : acc[f][r];
+  __syncthreads();
+
+  // 1024 outputs (4 frags x 64 lanes x 4 regs), one per thread.
+  const int f = tid >> 8;
+  const int l = (tid >> 2) & 63;
+  const int r = tid & 3;
+  const int t = f * 16 + (l & 15);
+  const int ch = n0 + 4 * (l >> 4) + r;
+  if (t >= M || ch >= N) return;
+  if constexpr (GROUPED) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += u2f((unsigned)red[w][f][l][r]);
+    ((unsigned short *)out)[(int64_t)t * ld_y + ch] = float_to_half_bits(sum);
+  } else {
+    int sum = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += red[w][f][l][r];
+    if constexpr (OUT_I32) {
+      ((int32_t *)out)[(int64_t)t * N + ch] = sum >> 8;
+    } else {
+      const float val = (float)sum * (sa[t] * sw[ch] * (1.0f / 256.0f));
+      ((unsigned short *)out)[(int64_t)t * ld_y + ch] = float_to_half_bits(val);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_decode(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,
+                              int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
+                              bool out_i32, hipStream_t stream) {
+  dim3 grid((unsigned)((N + kNT - 1) / kNT)), block(64 * kWaves);
+  if (group == 0) {
+    if (out_i32)
+      gemm_decode_kernel<false, true><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, 0, y, ld_y);
+    else
+      gemm_decode_kernel<false, false><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, 0, y, ld_y);
+  } else {
+    if (out_i32)
+      gemm_decode_kernel<true, true><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y);
+    else
+      gemm_decode_kernel<true, false><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qr

@@ -1,0 +1,145 @@
+// Head-wise rotated asymmetric 4-bit KV-cache quantization, head_dim 128.
+//
+// Method: QuaRot abstract (the KV cache in 4 bits, with the rotation applied
+// to it); DuQuant page, Knowl 12 (fixed Hadamard rotation +-1/sqrt(2^n),
+// per-token / per-head asymmetric quantization; step
+// (gamma max - beta min)/(2^b - 1) with gamma = beta = 1, b = 4).
+//
+// Per (token, head) vector v of 128 fp16:
+//   u = (v * signs) H_128            (unnormalised; y = u / sqrt(128))
+//   lo = min(min u, 0), hi = max(max u, 0)
+//   step = (hi - lo) / (15 sqrt(128)), z = rint(-lo * 15/(hi - lo)),
+//   q = clamp(rint(u * 15/(hi - lo)) + z, 0, 15)
+//
+// The whole 128-point transform is one pass of v_mfma_f32_16x16x32_f16
+// (input fp16 is exact, H entries +-1 are exact, sums in fp32): A = 16
+// vectors x 128 (one 16-byte load per lane per k-step), B = H_128 held in
+// registers with its columns permuted so that lane (c16, g) receives outputs
+// j = 8*c16 + nt for the 8 N-tiles nt - eight consecutive outputs per lane,
+// packed into one 32-bit word of codes per vector.
+#include "qr_common.h"
+#include "qr_launch.h"
+
+namespace qr {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+__global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
+    const unsigned short *__restrict__ kv, int64_t T, int H, int64_t ld_kv, const int8_t *__restrict__ signs,
+    uint8_t *__restrict__ codes, float *__restrict__ scales, uint8_t *__restrict__ zeros, float step_mul) {
+  const int lane = threadIdx.x & 63;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+
+  // B[s][nt]: slot j holds H[k][jj], k = 32 s + 8 g + j, jj = 8 c16 + nt.
+  v8h bop[4][8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = 32 * s + 8 * g + j;
+        const int jj = 8 * c16 + nt;
+        bop[s][nt][j] = (__builtin_popcount(k & jj) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+      }
+  unsigned smask[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int k = 32 * s + 8 * g + 2 * d;
+      smask[s][d] = signs == nullptr ? 0u
+                                     : ((signs[k] < 0 ? 0x8000u : 0u) | (signs[k + 1] < 0 ? 0x80000000u : 0u));
+    }
+
+  const int64_t nvec = T * (int64_t)H;
+  const int64_t ntiles = (nvec + 15) / 16;
+  const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerBlock;
+  const unsigned magic = f2u(kRoundMagic);
+
+  for (int64_t tile = wave_id; tile < ntiles; tile += wave_stride) {
+    // A: this lane loads row c16 of the tile (vector v), k-range 8 g + 32 s.
+    const int64_t v = tile * 16 + c16;
+    const bool valid = v < nvec;
+    const int64_t vt = valid ? v / H : 0;
+    const int vh = valid ? (int)(v - vt * H) : 0;
+    const unsigned short *src = kv + vt * ld_kv + vh * 128 + 8 * g;
+    v4u raw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      raw[s] = valid ? __builtin_nontemporal_load((const v4u *)(src + 32 * s)) : v4u{0u, 0u, 0u, 0u};
+
+    v4f c[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) c[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v4u w = raw[s];
+      w[0] ^= smask[s][0];
+      w[1] ^= smask[s][1];
+      w[2] ^= smask[s][2];
+      w[3] ^= smask[s][3];
+      const v8h a = __builtin_bit_cast(v8h, w);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[s][nt], c[nt], 0, 0, 0);
+    }
+
+    // Output vector row 4 g + r of the tile, outputs 8 c16 + nt.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float mn = 0.f, mx = 0.f;  // range widened to include 0
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        mn = fminf(mn, c[nt][r]);
+        mx = fmaxf(mx, c[nt][r]);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      }
+      const float rng = mx - mn;
+      const float inv = rng > 0.f ? 15.0f / rng : 0.f;
+      const int z = rng > 0.f ? (int)rintf(-mn * inv) : 0;
+      const unsigned bias = magic - (unsigned)z;  // bits(fma) - bias = rint(u*inv) + z
+      unsigned word = 0;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        int q = (int)(round_bits(c[nt][r], inv) - bias);
+        q = min(15, max(0, q));
+        word |= (unsigned)q << (4 * nt);
+      }
+      const int64_t vo = tile * 16 + 4 * g + r;
+      if (vo < nvec) {
+        *(unsigned *)(codes + vo * 64 + 4 * c16) = word;
+        if (c16 == 0) {
+          scales[vo] = rng * step_mul;
+          zeros[vo] = (uint8_t)z;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_quant(const void *kv, int64_t T, int64_t H, int64_t ld_kv, const int8_t *signs,
+                           uint8_t *codes, float *scales, uint8_t *zeros, hipStream_t stream) {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int cus = 256;
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t tiles = (T * H + 15) / 16;
+  const int64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t cap = (int64_t)cus * 8;
+  const int64_t grid = blocks < cap ? blocks : cap;
+  const float step_mul = (float)(1.0 / (15.0 * __builtin_sqrt(128.0)));
+  kv_quant_kernel<<<dim3((unsigned)grid), dim3(64 * kWavesPerBlock), 0, stream>>>(
+      (const unsigned short *)kv, T, (int)H, ld_kv, signs, codes, scales, zeros, step_mul);
+  return hipGetLastError();
+}
+
+}  // namespace qr

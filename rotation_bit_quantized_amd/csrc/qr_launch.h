@@ -1,0 +1,47 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+// Arguments have been validated by the caller; these only pick a grid and
+// launch on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qr {
+
+struct RotArgs {
+  int n;          // row width
+  int had_n;      // power-of-two Hadamard size
+  int dense_m;    // 1 or the dense factor size
+  const float *dense;
+  const int8_t *signs;
+};
+
+// Rotate + quantize, any validated shape (LDS-resident row, one block per row).
+hipError_t launch_rq_generic(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
+                             uint8_t *codes, float *scales, hipStream_t stream);
+
+// Rotate + quantize for n in {4096, 8192}, no dense factor, group 0 or 128
+// (first Hadamard factor on fp16 MFMA, the rest in registers, one wave per row).
+bool rq_pow2_supported(const RotArgs &r, int group);
+hipError_t launch_rq_pow2(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
+                          uint8_t *codes, float *scales, hipStream_t stream);
+
+// Rotate + quantize for n = 64 * m with a dense m x m factor (m <= 176),
+// dense factor on fp16 MFMA (hi/lo split), 64-point Hadamard in registers.
+bool rq_kron_supported(const RotArgs &r, int group);
+hipError_t launch_rq_kron(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
+                          uint8_t *codes, float *scales, hipStream_t stream);
+
+// Integer GEMM.  out_i32 == false: fp16 output with ld_y; true: int32 sums.
+hipError_t launch_gemm_prefill(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,
+                               int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
+                               bool out_i32, hipStream_t stream);
+hipError_t launch_gemm_decode(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,
+                              int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
+                              bool out_i32, hipStream_t stream);
+
+// KV-cache quantizer, head_dim 128.
+hipError_t launch_kv_quant(const void *kv, int64_t T, int64_t H, int64_t ld_kv, const int8_t *signs,
+                           uint8_t *codes, float *scales, uint8_t *zeros, hipStream_t stream);
+
+}  // namespace qr

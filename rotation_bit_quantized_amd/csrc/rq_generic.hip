@@ -1,0 +1,124 @@
+// Rotate + symmetric 4-bit RTN + pack, for any row width the ABI accepts.
+//
+// One workgroup owns one token row at a time (grid-stride over rows).  The
+// row is staged in LDS as fp32:
+//   1. x * signs                       (the random diagonal D, input side)
+//   2. dense factor: t[i*m + b] = sum_a x[i*m + a] O[a][b]   (if m > 1)
+//   3. Walsh-Hadamard butterflies over the Hadamard index i, in place
+//   4. max |.| per row or per group, s = max / (7 sqrt(p)), codes
+//      rint(v * 7 / max), packed two per byte.
+// This is the reference-shape path of the library: small or unusual widths
+// (n = 2 .. 16384, any power-of-two Hadamard size, dense factors up to 256).
+// The wide power-of-two and the 64 x m Kronecker shapes have MFMA kernels.
+//
+// Method: QuaRot summary (Elamur Research), "Key points" (RTN on the fly,
+// group 128); Hadamard normalisation +-1/sqrt(2^n): DuQuant page, Knowl 12;
+// Kronecker construction: QuIP summary, QuIP# quote.
+#include "qr_common.h"
+#include "qr_launch.h"
+
+namespace qr {
+namespace {
+
+constexpr int kBlock = 256;
+
+__global__ __launch_bounds__(kBlock) void rq_generic_kernel(
+    const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, int n, int had_n, int dense_m,
+    const float *__restrict__ dense, const int8_t *__restrict__ signs, int group,
+    uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
+  extern __shared__ float smem[];
+  float *buf = smem;
+  float *tmp = smem + n;
+  const int g = group ? group : n;
+  const int ngroups = n / g;
+  float *red = smem + (dense_m > 1 ? 2 * n : n);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  constexpr int kWaves = kBlock / 64;
+
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const unsigned short *xr = x + row * ld_x;
+    for (int k = tid; k < n; k += kBlock) {
+      float v = half_bits_to_float(xr[k]);
+      if (signs != nullptr && signs[k] < 0) v = -v;
+      buf[k] = v;
+    }
+    __syncthreads();
+
+    float *cur = buf;
+    if (dense_m > 1) {
+      for (int idx = tid; idx < n; idx += kBlock) {
+        const int i = idx / dense_m;
+        const int b = idx - i * dense_m;
+        const float *xi = buf + i * dense_m;
+        float acc = 0.f;
+        for (int a = 0; a < dense_m; ++a) acc = __builtin_fmaf(xi[a], dense[a * dense_m + b], acc);
+        tmp[idx] = acc;
+      }
+      __syncthreads();
+      cur = tmp;
+    }
+
+    // Butterflies over the Hadamard index i (stride dense_m in memory).
+    for (int h = 1; h < had_n; h <<= 1) {
+      for (int q = tid; q < n / 2; q += kBlock) {
+        const int j = q / dense_m;
+        const int b = q - j * dense_m;
+        const int i = (j / h) * 2 * h + (j % h);
+        float *p0 = cur + i * dense_m + b;
+        float *p1 = p0 + h * dense_m;
+        const float u = *p0, v = *p1;
+        *p0 = u + v;
+        *p1 = u - v;
+      }
+      __syncthreads();
+    }
+
+    // Max |y| of every group (or of the row): one wave per group.
+    for (int s = wave; s < ngroups; s += kWaves) {
+      float m = 0.f;
+      for (int k = lane; k < g; k += 64) m = fmaxf(m, fabsf(cur[s * g + k]));
+      m = wave_max(m);
+      if (lane == 0) red[s] = m;
+    }
+    __syncthreads();
+
+    uint8_t *cr = codes + row * (int64_t)(n / 2);
+    for (int c = tid; c < n / 2; c += kBlock) {
+      const int k = 2 * c;
+      const float m0 = red[k / g];
+      const float m1 = red[(k + 1) / g];
+      const float i0 = m0 > 0.f ? 7.0f / m0 : 0.f;
+      const float i1 = m1 > 0.f ? 7.0f / m1 : 0.f;
+      int q0 = (int)rintf(cur[k] * i0);
+      int q1 = (int)rintf(cur[k + 1] * i1);
+      q0 = min(7, max(-8, q0));
+      q1 = min(7, max(-8, q1));
+      cr[c] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
+    }
+    for (int s = tid; s < ngroups; s += kBlock) scales[row * ngroups + s] = red[s] * scale_mul;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rq_generic(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
+                             uint8_t *codes, float *scales, hipStream_t stream) {
+  const int g = group ? group : r.n;
+  const size_t lds = sizeof(float) * ((r.dense_m > 1 ? 2 * (size_t)r.n : (size_t)r.n) + (size_t)(r.n / g));
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void *)rq_generic_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t grid = rows < 4096 ? rows : 4096;
+  const float scale_mul = (float)(1.0 / (7.0 * __builtin_sqrt((double)r.had_n)));
+  rq_generic_kernel<<<dim3((unsigned)grid), dim3(kBlock), lds, stream>>>(
+      (const unsigned short *)x, rows, ld_x, r.n, r.had_n, r.dense_m, r.dense, r.signs, group, codes,
+      scales, scale_mul);
+  return hipGetLastError();
+}
+
+}  // namespace qr

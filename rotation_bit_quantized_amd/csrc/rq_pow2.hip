@@ -1,0 +1,254 @@
+// Online randomized Hadamard rotation + symmetric 4-bit RTN + nibble packing
+// for n = 2^L, L in {12, 13} (LLaMA hidden sizes 4096 and 8192), no dense
+// factor, per-row or group-128 scales.
+//
+// Method: y = (x * d) H_n / sqrt(n) (QuaRot summary, "Summary"; randomized
+// Hadamard: QuaRot press article), s = max|y|/7, q = rint(y/s) packed two per
+// byte (QuaRot summary, "Key points": RTN on the fly; group size 128).
+//
+// Design (one wave per token row, rows grid-strided over a persistent grid):
+//  * Element index bits e0..e(L-1).  Since H_n[e][f] = (-1)^popcount(e & f),
+//    the transform factors over any split of the bits into two sets; here
+//      i_b = {e0, e1, e6, e7, e8, e9}   (64-point factor, on MFMA)
+//      i_a = {e2..e5, e10..e(L-1)}       (the rest, in registers)
+//  * Pass 1: v_mfma_f32_16x16x32_f16 with A = the fp16 input (exact, sign-
+//    flipped by XOR) and B = the +-1 64-point factor.  Each lane loads 8-byte
+//    pieces: lane bits 0..3 select e2..e5 (rows of A), lane bits 4..5 select
+//    e6, e7 (k-groups), the two 8-byte halves select e8, the k-step e9 and the
+//    M-tile e10.. - so every load instruction reads 512 contiguous bytes.
+//  * B's columns are permuted so that the MFMA output puts e0, e1 in the
+//    N-tile index and e6..e9 in lane bits 0..3; the output rows carry e2, e3
+//    in the register index and e4, e5 in lane bits 4, 5.
+//  * Pass 2: butterflies on e2, e3, e10.. in registers; e4 and e5 are first
+//    swapped into registers with v_permlane16_swap / v_permlane32_swap (each
+//    a 2x2 transpose of a lane bit and a register bit), then butterflied.
+//  * After pass 2 each lane holds 64 consecutive outputs (two runs for
+//    n = 8192) and lane l owns outputs [64 l, 64 l + 64): absmax, rounding
+//    and packing stay in the lane and the codes go out as 16-byte stores.
+// The 1/sqrt(n) is folded into the stored scale (codes do not depend on it).
+#include "qr_common.h"
+#include "qr_launch.h"
+
+namespace qr {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+__device__ __forceinline__ void swap16(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane16_swap(f2u(a), f2u(b), false, false);
+  a = u2f(r[0]);
+  b = u2f(r[1]);
+}
+__device__ __forceinline__ void swap32(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane32_swap(f2u(a), f2u(b), false, false);
+  a = u2f(r[0]);
+  b = u2f(r[1]);
+}
+
+// Register index of a value: bits 0-1 = r (MFMA output row within the 4-row
+// group), bits 2-3 = N-tile, bits 4.. = M-tile.
+template <int L, int GROUP>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void rq_pow2_kernel(
+    const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, const int8_t *__restrict__ signs,
+    uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
+  constexpr int n = 1 << L;
+  constexpr int MT = 1 << (L - 10);  // M-tiles of 16 rows of the 64-column view
+  constexpr int NV = MT * 16;        // values per lane
+  static_assert(L == 12 || L == 13, "pass-2 layout written for n = 4096, 8192");
+
+  const int lane = threadIdx.x & 63;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+
+  // B operands: b[s][nt][j] = H(k, col), k bits from (slot j, k-group g, step
+  // s), column bits from (N-tile nt, lane column c16).
+  v8h bop[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int par = __builtin_popcount((j & 3) & nt) + __builtin_popcount(g & (c16 & 3)) +
+                        ((j >> 2) & (c16 >> 2) & 1) + (s & (c16 >> 3));
+        bop[s][nt][j] = (par & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+      }
+
+  // Sign masks for the pieces this lane loads: piece (m, s, h) covers
+  // elements base + 0..3 with base = 4 c16 + 64 g + 256 h + 512 s + 1024 m.
+  unsigned smask[MT][2][2][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int base = 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m;
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          unsigned mk = 0;
+          if (signs != nullptr) {
+            mk = (signs[base + 2 * d] < 0 ? 0x8000u : 0u) | (signs[base + 2 * d + 1] < 0 ? 0x80000000u : 0u);
+          }
+          smask[m][s][h][d] = mk;
+        }
+      }
+
+  const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerBlock;
+
+  for (int64_t row = wave_id; row < rows; row += wave_stride) {
+    const unsigned short *xr = x + row * ld_x;
+
+    // ---- loads (all issued before the first MFMA)
+    v2u piece[MT][2][2];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int base = 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m;
+          piece[m][s][h] = __builtin_nontemporal_load((const v2u *)(xr + base));
+        }
+
+    // ---- pass 1: 64-point factor on MFMA
+    float v[NV];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      v8h a[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        v4u w;
+        w[0] = piece[m][s][0][0] ^ smask[m][s][0][0];
+        w[1] = piece[m][s][0][1] ^ smask[m][s][0][1];
+        w[2] = piece[m][s][1][0] ^ smask[m][s][1][0];
+        w[3] = piece[m][s][1][1] ^ smask[m][s][1][1];
+        a[s] = __builtin_bit_cast(v8h, w);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        v4f c = {0.f, 0.f, 0.f, 0.f};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], bop[0][nt], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], bop[1][nt], c, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[(m << 4) | (nt << 2) | r] = c[r];
+      }
+    }
+
+    // ---- pass 2: butterflies over i_a
+    // register bits 0, 1 (e2, e3) and the M-tile bits (e10..)
+#pragma unroll
+    for (int bit = 0; bit < L - 8; ++bit) {
+      const int rb = bit < 2 ? bit : bit + 2;  // skip the N-tile bits 2, 3
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (i & (1 << rb)) continue;
+        const float a = v[i], b = v[i | (1 << rb)];
+        v[i] = a + b;
+        v[i | (1 << rb)] = a - b;
+      }
+    }
+    // lane bit 4 (e4) <-> register bit 4 (M-tile bit 0, already transformed)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (i & 16) continue;
+      swap16(v[i], v[i | 16]);
+      const float a = v[i], b = v[i | 16];
+      v[i] = a + b;
+      v[i | 16] = a - b;
+    }
+    // lane bit 5 (e5) <-> register bit 5 (M-tile bit 1)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (i & 32) continue;
+      swap32(v[i], v[i | 32]);
+      const float a = v[i], b = v[i | 32];
+      v[i] = a + b;
+      v[i | 32] = a - b;
+    }
+
+    // Lane now owns outputs e = 64*lane + f(i) (+ 4096 * bit6 of i for L=13)
+    // with f(i) = ((i>>2)&3) | (i&3)<<2 | ((i>>4)&3)<<4.
+    constexpr int RUNS = NV / 64;
+    float amax[RUNS];
+#pragma unroll
+    for (int run = 0; run < RUNS; ++run) {
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) mx = fmaxf(mx, fabsf(v[run * 64 + i]));
+      amax[run] = mx;
+    }
+    if (GROUP == 0) {
+      float mx = amax[0];
+#pragma unroll
+      for (int run = 1; run < RUNS; ++run) mx = fmaxf(mx, amax[run]);
+      mx = wave_max(mx);
+#pragma unroll
+      for (int run = 0; run < RUNS; ++run) amax[run] = mx;
+      if (lane == 0) scales[row] = mx * scale_mul;
+    } else {
+      // a group of 128 spans lanes 2q, 2q+1 of one run
+#pragma unroll
+      for (int run = 0; run < RUNS; ++run) {
+        amax[run] = fmaxf(amax[run], __shfl_xor(amax[run], 1, 64));
+        if ((lane & 1) == 0) scales[row * (n / 128) + run * 32 + (lane >> 1)] = amax[run] * scale_mul;
+      }
+    }
+
+    uint8_t *cr = codes + row * (int64_t)(n / 2);
+#pragma unroll
+    for (int run = 0; run < RUNS; ++run) {
+      const float inv = amax[run] > 0.f ? 7.0f / amax[run] : 0.f;
+      unsigned words[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        unsigned bits[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int e = 8 * w + t;  // position within the 64-run
+          const int i = ((e >> 2) & 3) | ((e & 3) << 2) | (((e >> 4) & 3) << 4);
+          bits[t] = round_bits(v[run * 64 + i], inv);
+        }
+        words[w] = pack8_nibbles(bits[0], bits[1], bits[2], bits[3], bits[4], bits[5], bits[6], bits[7]);
+      }
+      v4u *dst = (v4u *)(cr + run * (n / 4) + 32 * lane);
+      dst[0] = v4u{words[0], words[1], words[2], words[3]};
+      dst[1] = v4u{words[4], words[5], words[6], words[7]};
+    }
+  }
+}
+
+template <int L, int GROUP>
+hipError_t launch_one(const void *x, int64_t rows, int64_t ld_x, const int8_t *signs, uint8_t *codes,
+                      float *scales, hipStream_t stream) {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int cus = 256;
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t blocks_needed = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t cap = (int64_t)cus * 8;
+  const int64_t grid = blocks_needed < cap ? blocks_needed : cap;
+  const float scale_mul = (float)(1.0 / (7.0 * __builtin_sqrt((double)(1 << L))));
+  rq_pow2_kernel<L, GROUP><<<dim3((unsigned)grid), dim3(64 * kWavesPerBlock), 0, stream>>>(
+      (const unsigned short *)x, rows, ld_x, signs, codes, scales, scale_mul);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool rq_pow2_supported(const RotArgs &r, int group) {
+  return r.dense_m == 1 && (r.n == 4096 || r.n == 8192) && (group == 0 || group == 128);
+}
+
+hipError_t launch_rq_pow2(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
+                          uint8_t *codes, float *scales, hipStream_t stream) {
+  if (r.n == 4096) {
+    return group ? launch_one<12, 128>(x, rows, ld_x, r.signs, codes, scales, stream)
+                 : launch_one<12, 0>(x, rows, ld_x, r.signs, codes, scales, stream);
+  }
+  return group ? launch_one<13, 128>(x, rows, ld_x, r.signs, codes, scales, stream)
+               : launch_one<13, 0>(x, rows, ld_x, r.signs, codes, scales, stream);
+}
+
+}  // namespace qr

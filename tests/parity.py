@@ -1,0 +1,90 @@
+"""Parity helpers shared by the GPU tests: compare library results with the
+CPU oracle under the stated tolerances.
+
+* Quantized codes: identical, except where the oracle's pre-rounding value
+  lies within BOUNDARY_WINDOW of a .5 rounding boundary; such mismatches are
+  counted and must not exceed MAX_MISMATCH_FRAC of the elements.  (The GPU
+  forms the rotated value in fp32, the oracle in fp64; only values that sit
+  on a rounding boundary to within fp32 error can round differently.)
+* Integer GEMM sums: bit-exact.
+* fp16 outputs: relative Frobenius error <= OUT_REL_FRO against the oracle's
+  fp64 dequantized output from the oracle's codes.
+* Scales: relative error <= SCALE_RTOL (fp32 transform vs fp64).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+
+BOUNDARY_WINDOW = 1e-3
+MAX_MISMATCH_FRAC = 1e-4
+OUT_REL_FRO = 2e-3
+SCALE_RTOL = 1e-5
+
+
+def near_half(t: np.ndarray) -> np.ndarray:
+    """Pre-rounding values within BOUNDARY_WINDOW of a .5 boundary."""
+    return np.abs(np.abs(t - np.floor(t)) - 0.5) < BOUNDARY_WINDOW
+
+
+def check_symmetric_codes(gpu_packed: np.ndarray, q_or: np.ndarray, t_or: np.ndarray, what: str = "codes"):
+    g = O.unpack_int4(gpu_packed)
+    assert g.shape == q_or.shape, (g.shape, q_or.shape)
+    mism = g != q_or
+    bad = mism & ~near_half(t_or)
+    nm, nb = int(mism.sum()), int(bad.sum())
+    assert nb == 0, f"{what}: {nb} mismatches away from a rounding boundary (first at {np.argwhere(bad)[:5].tolist()})"
+    assert nm <= MAX_MISMATCH_FRAC * mism.size, f"{what}: {nm} boundary mismatches of {mism.size}"
+    # a boundary mismatch can only be off by one
+    if nm:
+        assert np.abs(g[mism].astype(int) - q_or[mism].astype(int)).max() == 1
+    return nm
+
+
+def check_scales(gpu: np.ndarray, ref: np.ndarray, what: str = "scales"):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    zero = ref == 0
+    assert np.all(gpu[zero] == 0), f"{what}: nonzero scale for an all-zero row/group"
+    rel = np.abs(gpu[~zero] - ref[~zero]) / ref[~zero]
+    assert rel.size == 0 or rel.max() <= SCALE_RTOL, f"{what}: max rel err {rel.max():.3e}"
+
+
+def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a))
+
+
+def check_output(gpu_fp16: np.ndarray, ref: np.ndarray, what: str = "output"):
+    e = rel_fro(gpu_fp16.astype(np.float64), ref)
+    assert e <= OUT_REL_FRO, f"{what}: relative Frobenius error {e:.3e}"
+    return e
+
+
+def check_kv(gpu_codes, gpu_step, gpu_zero, kv, signs=None):
+    """KV parity: steps to SCALE_RTOL, zero points exact except where -lo/step
+    is on a .5 boundary, codes exact except on a boundary; vectors whose zero
+    point legitimately differs are checked by the reconstruction bound."""
+    q_or, st_or, z_or, t_or, zt_or = O.kv_quantize(kv, signs)
+    T, H, D = kv.shape
+    g = O.unpack_uint4(gpu_codes.reshape(T, H, D // 2))
+    check_scales(gpu_step, st_or, "kv step")
+    zg = gpu_zero.astype(np.int64)
+    zmis = zg != z_or
+    assert np.all(near_half(zt_or)[zmis]), "kv zero point differs away from a rounding boundary"
+    assert zmis.sum() <= max(1, MAX_MISMATCH_FRAC * zmis.size)
+    same = ~zmis
+    mism = (g != q_or) & same[..., None]
+    bad = mism & ~near_half(t_or)
+    assert int(bad.sum()) == 0, f"kv codes: {int(bad.sum())} mismatches away from a boundary"
+    assert int(mism.sum()) <= MAX_MISMATCH_FRAC * mism.size
+    if zmis.any():
+        y = kv.astype(np.float64) @ O.rotation_matrix(D, D, signs=signs)
+        rec = (g.astype(np.float64) - zg[..., None]) * np.asarray(gpu_step, np.float64)[..., None]
+        err = np.abs(rec - y)[zmis]
+        assert np.all(err <= (np.asarray(gpu_step, np.float64)[zmis][:, None] * (1.0 + 1e-4)))
+    return int(mism.sum()), int(zmis.sum())

@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/qr.h declares, and
+reject bad arguments on the host with the documented status before anything
+is launched (these calls never reach the device, so they run on the CPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rotation_bit_quantized_amd as qr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qr.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(qr.library_path()), reason="libqr.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qr_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(qr.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qr.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {qr.library_path()}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_status_strings_and_version():
+    for s in range(5):
+        assert qr.status_str(s)
+    assert qr.status_str(99) == "unknown status"
+    assert qr.version() >= 100
+
+
+def rot(n=4096, had=4096, m=1, dense=None, signs=None):
+    return qr._Rot(n, had, m, dense, signs)
+
+
+A16 = 0x10000      # a fake, 16-byte-aligned device address: never dereferenced, the calls below fail validation
+MIS = 0x10001
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(x=None), qr.QR_EINVAL),
+    (dict(rows=-1), qr.QR_EINVAL),
+    (dict(ld=4095), qr.QR_ESHAPE),
+    (dict(ld=4100), qr.QR_EALIGN),
+    (dict(group=100), qr.QR_ESHAPE),
+    (dict(group=16), qr.QR_ESHAPE),
+    (dict(group=8192), qr.QR_ESHAPE),
+    (dict(x=MIS), qr.QR_EALIGN),
+    (dict(codes=MIS), qr.QR_EALIGN),
+    (dict(r=rot(n=4096, had=2048)), qr.QR_ESHAPE),
+    (dict(r=rot(n=12, had=12)), qr.QR_ESHAPE),
+    (dict(r=rot(n=16384 * 2, had=8192, m=4, dense=A16)), qr.QR_ESHAPE),
+    (dict(r=rot(n=64 * 172, had=64, m=172, dense=None)), qr.QR_EINVAL),
+    (dict(r=rot(n=4096, had=4096, m=1, dense=A16)), qr.QR_EINVAL),
+    (dict(r=rot(n=3, had=1, m=3, dense=A16)), qr.QR_ESHAPE),
+    (dict(r=None), qr.QR_EINVAL),
+])
+def test_rotate_quant_rejects(args, expect):
+    lib = qr.library()
+    r = args.get("r", rot())
+    rp = None if r is None else ctypes.byref(r)
+    st = lib.qr_rotate_quant(args.get("x", A16), args.get("rows", 4), args.get("ld", 4096), rp,
+                             args.get("group", 0), args.get("codes", A16), args.get("scales", A16), None)
+    assert st == expect
+
+
+def test_rotate_quant_zero_rows_is_noop():
+    assert qr.library().qr_rotate_quant(None, 0, 4096, ctypes.byref(rot()), 0, None, None, None) == qr.QR_OK
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(K=4000), qr.QR_ESHAPE),
+    (dict(K=0), qr.QR_EINVAL),
+    (dict(M=-1), qr.QR_EINVAL),
+    (dict(group=64), qr.QR_ESHAPE),
+    (dict(group=384), qr.QR_ESHAPE),
+    (dict(a=None), qr.QR_EINVAL),
+    (dict(a=MIS), qr.QR_EALIGN),
+    (dict(ld=100), qr.QR_ESHAPE),
+    (dict(y=None), qr.QR_EINVAL),
+])
+def test_gemm_rejects(args, expect):
+    lib = qr.library()
+    st = lib.qr_int4_gemm(args.get("a", A16), A16, A16, A16, args.get("M", 128), 256, args.get("K", 4096),
+                          args.get("group", 0), args.get("y", A16), args.get("ld", 256), None)
+    assert st == expect
+
+
+def test_gemm_empty_is_noop():
+    lib = qr.library()
+    assert lib.qr_int4_gemm(None, None, None, None, 0, 256, 4096, 0, None, 256, None) == qr.QR_OK
+    assert lib.qr_int4_gemm_i32(None, None, 5, 0, 4096, 0, None, None) == qr.QR_OK
+
+
+def test_gemm_i32_rejects():
+    lib = qr.library()
+    assert lib.qr_int4_gemm_i32(A16, A16, 4, 4, 4096, 0, None, None) == qr.QR_EINVAL
+    assert lib.qr_int4_gemm_i32(A16, A16, 4, 4, 4096, 0, MIS + 1, None) == qr.QR_EALIGN
+    assert lib.qr_int4_gemm_i32(A16, A16, 4, 4, 4097, 0, A16, None) == qr.QR_ESHAPE
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(D=64), qr.QR_ESHAPE),
+    (dict(T=-1), qr.QR_EINVAL),
+    (dict(ld=4000), qr.QR_ESHAPE),
+    (dict(ld=4100), qr.QR_EALIGN),
+    (dict(kv=MIS), qr.QR_EALIGN),
+    (dict(kv=None), qr.QR_EINVAL),
+    (dict(zeros=None), qr.QR_EINVAL),
+])
+def test_kv_rejects(args, expect):
+    lib = qr.library()
+    st = lib.qr_kv_quant(args.get("kv", A16), args.get("T", 4), 32, args.get("D", 128), args.get("ld", 4096),
+                         None, A16, A16, args.get("zeros", A16), None)
+    assert st == expect
+
+
+def test_kv_empty_is_noop():
+    assert qr.library().qr_kv_quant(None, 0, 32, 128, 4096, None, None, None, None, None) == qr.QR_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 4096, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        qr.rotate_quant(x, object())
