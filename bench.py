@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Throughput of QuaRot's 4-bit linear-layer hot path on one MI355X.
+
+One step = one pass of the whole path over one batch, all on one HIP stream:
+  qr_rotate_quant  x [M, K] fp16 -> int4 codes + per-token scales
+  qr_int4_gemm     codes x pre-rotated int4 weights -> y [M, N] fp16
+  qr_kv_quant      the K and V slices of y (fused QKV output), 32 heads x 128
+Default workload: LLaMA-2-7B fused QKV prefill, x 2048 x 4096 -> 12288 (the
+layer the QuaRot summary's prefill figures are about: batch 64 x 2048 tokens
+in one block).  Inputs are synthetic and seeded (package ``workloads``);
+weights are prepared on the GPU before timing (rotate + quantize the rows of
+W^T with the same library call).  To keep the measurement honest about HBM,
+steps cycle through enough distinct buffer sets (>= 1 GiB) that nothing is
+served from the 256 MB Infinity Cache between uses.
+
+Prints one JSON line.  `value` is whole-step throughput in TOPS (2 M N K per
+step).  `roofline` is for the dominant kernel (the int4 GEMM) with its
+average launch time from HIP events recorded around each launch on the
+launch stream.  `cpu_baseline` is the CPU oracle timed on a bounded row
+sample of the same workload.
+
+  python bench.py [--steps 20] [--warmup 5] [--config c2] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published (5.0 POP/s)
+CACHE_BYTES = 1 << 30        # cycle buffers over >= 1 GiB (MALL is 256 MB)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=["c2"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="token rows in the CPU oracle sample")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="also run one device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0 = enough for 1 GiB)")
+    return ap.parse_args()
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src_files, launches_bytes):
+    """HBM bytes of one launch from committed rocprofv3 counter runs, or None
+    when they are missing or the kernel source changed since they were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash(src_files):
+        return None
+    return {"fetch_bytes": rec["fetch_bytes"], "write_bytes": rec["write_bytes"],
+            "total_bytes": rec["fetch_bytes"] + rec["write_bytes"], "algorithmic_bytes": launches_bytes,
+            "calibration": rec.get("calibration")}
+
+
+def cpu_baseline(cfg, rows):
+    """The oracle on a bounded sample: `rows` token rows through rotate,
+    quantize, int64 GEMM against all N output channels, dequantize and the KV
+    quantizer on those rows' K and V slices.  Weight preparation (offline in
+    the method) is not timed."""
+    import oracle as O
+    import workloads as W
+    threads = len(os.sched_getaffinity(0))
+    x = W.make_x(cfg, rows=np.arange(rows))
+    w = W.make_w(cfg)
+    r = O.rotation_matrix(cfg.K, signs=W.make_signs(cfg))
+    qw, sw = O.quantize_weights(O.rotate_weights(w, r), cfg.group)
+    t0 = time.perf_counter()
+    y = O.rotate(x, r)
+    qx, sx, _ = O.quantize_symmetric(y, cfg.group)
+    blocks = np.array_split(np.arange(cfg.N), threads)
+    with cf.ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda b: O.int_gemm(qx, qw[b], cfg.group), blocks))
+    acc = np.concatenate(parts, axis=-1)
+    out = O.dequantize_output(acc, sx, sw, cfg.group)
+    hq = cfg.K  # K and V slices of the fused output: heads of 128
+    kv = out.astype(np.float16)
+    O.kv_quantize(kv[:, hq:2 * hq].reshape(rows, hq // 128, 128))
+    O.kv_quantize(kv[:, 2 * hq:3 * hq].reshape(rows, hq // 128, 128))
+    dt = time.perf_counter() - t0
+    ops = 2.0 * rows * cfg.N * cfg.K
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{rows} of {cfg.M} token rows: fp64 explicit-matrix rotation, RTN, int64 GEMM against "
+                      f"all {cfg.N} channels (column blocks over {threads} threads), fp64 dequant, KV quant of "
+                      f"the sampled rows' K/V; weight prep untimed"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+              f"(the hot path is per-token independent and would shard tokens across GPUs with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import rotation_bit_quantized_amd as qr
+
+    qr.library()                     # no fallback: fail loudly without the HIP library
+    cfg = W.CONFIGS[args.config]
+    M, N, K = cfg.M, cfg.N, cfg.K
+    H = K // 128
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------- resident inputs (untimed)
+    x_host = W.make_x(cfg)
+    w_host = W.make_w(cfg)
+    rot = qr.Rotation.hadamard(K, W.make_signs(cfg))
+    x0 = torch.from_numpy(x_host).to(dev)
+    wt = torch.from_numpy(np.ascontiguousarray(w_host.T)).to(dev)
+    wc0, ws0 = qr.rotate_quant(wt, rot, cfg.group)          # offline weight prep, on the GPU
+    del wt
+    set_bytes = (x0.numel() * 2 + M * K // 2 + M * 4 + wc0.numel() + ws0.numel() * 4 + M * N * 2
+                 + 2 * (M * H * 64 + M * H * 5))
+    nsets = args.sets or max(1, -(-CACHE_BYTES // set_bytes))
+    sets = []
+    for i in range(nsets):
+        s = dict(x=x0.clone(), wc=wc0.clone(), ws=ws0.clone(),
+                 xc=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                 xs=torch.empty((M,), dtype=torch.float32, device=dev),
+                 y=torch.empty((M, N), dtype=torch.float16, device=dev),
+                 kc=torch.empty((M, H, 64), dtype=torch.uint8, device=dev),
+                 ks=torch.empty((M, H), dtype=torch.float32, device=dev),
+                 kz=torch.empty((M, H), dtype=torch.uint8, device=dev),
+                 vc=torch.empty((M, H, 64), dtype=torch.uint8, device=dev),
+                 vs=torch.empty((M, H), dtype=torch.float32, device=dev),
+                 vz=torch.empty((M, H), dtype=torch.uint8, device=dev))
+        sets.append(s)
+    del x0, wc0, ws0
+    stream = torch.cuda.current_stream()
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        qr.rotate_quant(s["x"], rot, cfg.group, codes=s["xc"], scales=s["xs"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        qr.int4_gemm(s["xc"], s["xs"], s["wc"], s["ws"], cfg.group, y=s["y"], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        qr.kv_quant(s["y"][:, K:2 * K], codes=s["kc"], scales=s["ks"], zeros=s["kz"], stream=stream)
+        qr.kv_quant(s["y"][:, 2 * K:3 * K], codes=s["vc"], scales=s["vs"], zeros=s["vz"], stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    if args.copy_calib:
+        nb = args.copy_calib << 20
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    gpu_ms = evs[0][0].elapsed_time(evs[-1][3])        # first launch to last completion
+    ms_per_step = gpu_ms / args.steps
+    rq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    kv_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    ops = 2.0 * M * N * K
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    rq_bytes = M * K * 2 + M * K // 2 + M * 4
+    kv_bytes = 2 * (M * H * 128 * 2 + M * H * 64 + M * H * 5)
+    gemm_bytes = M * K // 2 + N * K // 2 + M * 4 + N * 4 + M * N * 2
+    traffic = load_traffic("int4_gemm_c2",
+                           ["rotation_bit_quantized_amd/csrc/gemm_prefill.hip",
+                            "rotation_bit_quantized_amd/csrc/qr_common.h"], gemm_bytes)
+
+    out = {
+        "metric": "rotate+quant+int4 GEMM TOPS and GB/s at 7B/70B layer shapes; % of roofline",
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.desc}; rotate D.H_{K} + per-token int4 RTN, int4 GEMM (int8 MFMA, "
+                        f"per-channel int4 weights, fp16 out), 4-bit KV quant of the K/V slices ({M}x{H}x128 each)",
+            "M": M, "N": N, "K": K, "group": cfg.group, "codes": "int4", "mfma": "int8 -> int32",
+            "rotation": "fp32 (fp16-MFMA first factor)", "buffer_sets": nsets,
+        },
+        "kernels": {
+            "rotate_quant": {"us": round(rq_ms * 1e3, 3), "GB/s": round(rq_bytes / (rq_ms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(rq_bytes / (rq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "bytes": rq_bytes},
+            "int4_gemm": {"us": round(gemm_ms * 1e3, 3), "TOPS": round(gemm_tops, 2),
+                          "frac_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4), "bytes": gemm_bytes},
+            "kv_quant_KV": {"us": round(kv_ms * 1e3, 3), "GB/s": round(kv_bytes / (kv_ms * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(kv_bytes / (kv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "bytes": kv_bytes},
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "int4_gemm (gemm_prefill_kernel)",
+            "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+            "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+            "traffic": None if traffic is None else traffic["total_bytes"],
+            "traffic_detail": traffic,
+        },
+        "wall_s": round(wall, 4),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_rows, M))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -63,7 +63,7 @@ typedef enum {
  * dense index is the fastest: element k = i * dense_m + a.
  *
  * Fields: n = had_n * dense_m, n even, 2 <= n <= 16384, had_n a power of two
- * in [1, 8192], dense_m in [1, 256].  `dense` (device, fp32, row-major
+ * in [1, 16384], dense_m in [1, 256].  `dense` (device, fp32, row-major
  * [dense_m][dense_m]) must be NULL iff dense_m == 1; the library does not
  * check that it is orthogonal.  `signs` (device, int8 [n], each +1 or -1)
  * may be NULL for D = I.

@@ -14,7 +14,7 @@ qr_status from_hip(hipError_t e) { return e == hipSuccess ? QR_OK : QR_EDEVICE; 
 qr_status check_rotation(const qr_rotation *rot) {
   if (rot == nullptr) return QR_EINVAL;
   if (rot->n <= 0 || rot->had_n <= 0 || rot->dense_m <= 0) return QR_EINVAL;
-  if (!pow2(rot->had_n) || rot->had_n > 8192) return QR_ESHAPE;
+  if (!pow2(rot->had_n) || rot->had_n > 16384) return QR_ESHAPE;
   if (rot->dense_m > 256) return QR_ESHAPE;
   if (rot->n != rot->had_n * rot->dense_m) return QR_ESHAPE;
   if (rot->n < 2 || rot->n > 16384 || (rot->n & 1)) return QR_ESHAPE;

@@ -28,14 +28,19 @@ def near_half(t: np.ndarray) -> np.ndarray:
     return np.abs(np.abs(t - np.floor(t)) - 0.5) < BOUNDARY_WINDOW
 
 
-def check_symmetric_codes(gpu_packed: np.ndarray, q_or: np.ndarray, t_or: np.ndarray, what: str = "codes"):
+def check_symmetric_codes(gpu_packed: np.ndarray, q_or: np.ndarray, t_or: np.ndarray, what: str = "codes",
+                          cap_count: bool = True):
+    """cap_count=False for hand-built inputs full of exact .5 ties (e.g. a
+    constant row under random signs), where every tie is a legitimate
+    boundary case and the workload-level count cap does not apply."""
     g = O.unpack_int4(gpu_packed)
     assert g.shape == q_or.shape, (g.shape, q_or.shape)
     mism = g != q_or
     bad = mism & ~near_half(t_or)
     nm, nb = int(mism.sum()), int(bad.sum())
     assert nb == 0, f"{what}: {nb} mismatches away from a rounding boundary (first at {np.argwhere(bad)[:5].tolist()})"
-    assert nm <= MAX_MISMATCH_FRAC * mism.size, f"{what}: {nm} boundary mismatches of {mism.size}"
+    if cap_count:
+        assert nm <= MAX_MISMATCH_FRAC * mism.size, f"{what}: {nm} boundary mismatches of {mism.size}"
     # a boundary mismatch can only be off by one
     if nm:
         assert np.abs(g[mism].astype(int) - q_or[mism].astype(int)).max() == 1
