@@ -49,10 +49,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2", choices=["c2"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="token rows in the CPU oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="token rows in the CPU oracle sample (0 = all)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0 = enough for 1 GiB)")
+    ap.add_argument("--suite", action="store_true",
+                    help="instead of the step, time each kernel at every config's shape (one JSON line each)")
+    ap.add_argument("--only", default="", help="with --suite: comma-separated case names to run")
     return ap.parse_args()
 
 
@@ -110,8 +113,117 @@ def cpu_baseline(cfg, rows):
                       f"the sampled rows' K/V; weight prep untimed"}
 
 
+def time_launches(fn, n, warm=3):
+    """Average duration (ms) of fn(i) over n launches, HIP events on the
+    current stream around the whole sequence."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def suite(args):
+    """Kernel-level throughput at each config's shape.  Buffers are cycled so
+    the data touched per launch comes from HBM, not the 256 MB cache, unless
+    the case is explicitly a latency (single-shot) case."""
+    import torch
+    import workloads as W
+    import rotation_bit_quantized_amd as qr
+    dev = torch.device("cuda:0")
+    only = set(filter(None, args.only.split(",")))
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+
+    def codes(rows, k):
+        return torch.randint(0, 256, (rows, k // 2), dtype=torch.uint8, device=dev, generator=g)
+
+    def emit(case, **kw):
+        print(json.dumps({"case": case, **kw}), flush=True)
+
+    def copies(make, per_bytes):
+        n = max(1, -(-CACHE_BYTES // max(1, per_bytes)))
+        return [make() for _ in range(n)]
+
+    def rq_case(name, cfg, rows, group, reps=20):
+        if only and name not in only:
+            return
+        c = W.CONFIGS[cfg]
+        x = torch.from_numpy(W.make_x(c, rows=np.arange(rows))).to(dev)
+        if c.dense_m > 1:
+            rot = qr.Rotation.kronecker(c.had_n, W.make_dense(c), W.make_signs(c))
+        else:
+            rot = qr.Rotation.hadamard(c.K, W.make_signs(c))
+        nbytes = rows * c.K * 2 + rows * c.K // 2 + rows * 4 * (1 if group == 0 else c.K // group)
+        xs = copies(lambda: x.clone(), rows * c.K * 2)
+        outs = [qr.rotate_quant(xx, rot, group) for xx in xs]
+        ms = time_launches(lambda i: qr.rotate_quant(xs[i % len(xs)], rot, group, *outs[i % len(xs)]), reps)
+        emit(name, kernel="qr_rotate_quant", shape=[rows, c.K], group=group, us=round(ms * 1e3, 3),
+             GBs=round(nbytes / ms / 1e6, 1), frac_hbm=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+             bytes=nbytes, buffers=len(xs))
+
+    def gemm_case(name, M, N, K, group, reps=10, stream_w=1):
+        if only and name not in only:
+            return
+        G = 1 if group == 0 else K // group
+        a = codes(M, K)
+        sa = torch.rand((M,) if group == 0 else (M, G), device=dev, generator=g) * 0.01
+        ws = [codes(N, K) for _ in range(stream_w)]
+        sw = torch.rand((N,) if group == 0 else (N, G), device=dev, generator=g) * 0.01
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ms = time_launches(lambda i: qr.int4_gemm(a, sa, ws[i % stream_w], sw, group, y=y), reps)
+        ops = 2.0 * M * N * K
+        nbytes = M * K // 2 + N * K // 2 + M * N * 2 + 4 * G * (M + N)
+        emit(name, kernel="qr_int4_gemm", shape=[M, N, K], group=group, us=round(ms * 1e3, 3),
+             TOPS=round(ops / ms / 1e9, 2), frac_int8=round(ops / ms / 1e9 / INT8_PEAK_TOPS, 4),
+             GBs=round(nbytes / ms / 1e6, 1), frac_hbm=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+             bytes=nbytes, weight_sets=stream_w)
+
+    def kv_case(name, T, reps=20, cycle=True):
+        if only and name not in only:
+            return
+        H = 32
+        if T <= 64:
+            k, _ = W.make_kv("c5")
+        else:
+            k = W.make_kv_large(T, H)
+        kt = torch.from_numpy(k).to(dev)
+        nbytes = T * H * (256 + 64 + 5)
+        ks = copies(lambda: kt.clone(), T * H * 256) if cycle else [kt]
+        outs = [qr.kv_quant(kk) for kk in ks]
+        ms = time_launches(lambda i: qr.kv_quant(ks[i % len(ks)], None, *outs[i % len(ks)]), reps)
+        emit(name, kernel="qr_kv_quant", shape=[T, H, 128], us=round(ms * 1e3, 3),
+             GBs=round(nbytes / ms / 1e6, 1), frac_hbm=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+             bytes=nbytes, buffers=len(ks))
+
+    rq_case("rq_c2", "c2", 2048, 0)
+    rq_case("rq_c4_g128", "c4", 16384, 128)
+    rq_case("rq_c5", "c5", 64, 0)
+    gemm_case("gemm_c2", 2048, 12288, 4096, 0)
+    gemm_case("gemm_c3", 131072, 4096, 11008, 0, reps=3)
+    gemm_case("gemm_c4_g128", 16384, 28672, 8192, 128, reps=3)
+    gemm_case("gemm_c5_decode_single", 64, 4096, 4096, 0, reps=50)
+    gemm_case("gemm_c5_decode_streamed", 64, 4096, 4096, 0, reps=128, stream_w=64)
+    kv_case("kv_c5_decode", 64, reps=50, cycle=False)
+    kv_case("kv_prefill_131072", 131072, reps=5)
+
+
 def main():
     args = parse()
+    if args.suite:
+        import torch
+        import rotation_bit_quantized_amd as qr
+        qr.library()
+        torch.cuda.set_device(0)
+        suite(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
               f"(the hot path is per-token independent and would shard tokens across GPUs with no exchange).",
@@ -245,7 +357,7 @@ def main():
         "wall_s": round(wall, 4),
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_rows, M))
+        out["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_rows or M, M))
     print(json.dumps(out), flush=True)
 
 

@@ -65,8 +65,8 @@ typedef enum {
  * Fields: n = had_n * dense_m, n even, 2 <= n <= 16384, had_n a power of two
  * in [1, 16384], dense_m in [1, 256].  `dense` (device, fp32, row-major
  * [dense_m][dense_m]) must be NULL iff dense_m == 1; the library does not
- * check that it is orthogonal.  `signs` (device, int8 [n], each +1 or -1)
- * may be NULL for D = I.
+ * check that it is orthogonal.  `signs` (device, int8 [n], each +1 or -1,
+ * 4-byte aligned) may be NULL for D = I.
  */
 typedef struct {
   int64_t n;
@@ -120,7 +120,7 @@ qr_status qr_rotate_quant(const void *x_f16, int64_t rows, int64_t ld_x,
  * w_scales  device, fp32 [N] or [N][K/group]
  * M, N >= 0; K > 0 and a multiple of 128; group 0 or a multiple of 128 that
  * divides K.
- * y_f16     device, fp16 [M][ld_y], ld_y >= N, ld_y even, 4-byte aligned.
+ * y_f16     device, fp16 [M][ld_y], ld_y >= N, 2-byte aligned.
  *
  * M <= 64 runs the memory-bound decode kernel (weights streamed once); larger
  * M runs the MFMA-bound prefill kernel.  Both give identical integer sums.
@@ -148,7 +148,7 @@ qr_status qr_int4_gemm(const uint8_t *a_codes, const float *a_scales,
  *         ld_kv >= H * head_dim, multiple of 8; 16-byte aligned.  This lets
  *         the K or V slice of a fused QKV output be quantized in place.
  * T, H    >= 0; head_dim == 128.
- * signs   device int8 [head_dim] of +-1, or NULL.
+ * signs   device int8 [head_dim] of +-1 (4-byte aligned), or NULL.
  * codes   device [T][H][head_dim/2] unsigned packed codes (16-byte aligned)
  * scales  device fp32 [T][H] (the step)
  * zeros   device uint8 [T][H] (the zero point z)

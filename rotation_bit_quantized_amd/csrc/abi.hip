@@ -62,7 +62,7 @@ qr_status qr_rotate_quant(const void *x_f16, int64_t rows, int64_t ld_x, const q
   if (rows == 0) return QR_OK;
   if (x_f16 == nullptr || codes == nullptr || scales == nullptr) return QR_EINVAL;
   if (!aligned(x_f16, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return QR_EALIGN;
-  if (rot->signs != nullptr && !aligned(rot->signs, 1)) return QR_EALIGN;
+  if (rot->signs != nullptr && !aligned(rot->signs, 4)) return QR_EALIGN;
 
   qr::RotArgs r{(int)rot->n, (int)rot->had_n, (int)rot->dense_m, rot->dense, rot->signs};
   hipStream_t s = (hipStream_t)stream;
@@ -115,6 +115,7 @@ qr_status qr_kv_quant(const void *kv_f16, int64_t T, int64_t H, int64_t head_dim
   if (T == 0 || H == 0) return QR_OK;
   if (kv_f16 == nullptr || codes == nullptr || scales == nullptr || zeros == nullptr) return QR_EINVAL;
   if (!aligned(kv_f16, 16) || !aligned(codes, 4) || !aligned(scales, 4)) return QR_EALIGN;
+  if (signs != nullptr && !aligned(signs, 4)) return QR_EALIGN;
   return from_hip(qr::launch_kv_quant(kv_f16, T, H, ld_kv, signs, codes, scales, zeros, (hipStream_t)stream));
 }
 

@@ -44,15 +44,24 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
         const int jj = 8 * c16 + nt;
         bop[s][nt][j] = (__builtin_popcount(k & jj) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
       }
+  // sign masks for this lane's k-range 32 s + 8 g + 0..7 (two aligned words)
   unsigned smask[4][4];
+  if (signs != nullptr) {
+    unsigned sw[4][2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const int k = 32 * s + 8 * g + 2 * d;
-      smask[s][d] = signs == nullptr ? 0u
-                                     : ((signs[k] < 0 ? 0x8000u : 0u) | (signs[k + 1] < 0 ? 0x80000000u : 0u));
-    }
+      for (int d = 0; d < 2; ++d) sw[s][d] = *(const unsigned *)(signs + 32 * s + 8 * g + 4 * d);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int d = 0; d < 2; ++d) sign_masks4(sw[s][d], smask[s][2 * d], smask[s][2 * d + 1]);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) smask[s][d] = 0u;
+  }
 
   const int64_t nvec = T * (int64_t)H;
   const int64_t ntiles = (nvec + 15) / 16;

@@ -44,6 +44,14 @@ __device__ __forceinline__ unsigned short float_to_half_bits(float f) {
   return __builtin_bit_cast(unsigned short, (_Float16)f);
 }
 
+// XOR masks that flip the fp16 sign of elements whose int8 sign is negative,
+// for four consecutive int8 signs packed in one word: elements 0, 1 go to
+// (bit 15, bit 31) of m01, elements 2, 3 to those of m23.
+__device__ __forceinline__ void sign_masks4(unsigned w, unsigned &m01, unsigned &m23) {
+  m01 = ((w & 0x80u) << 8) | ((w & 0x8000u) << 16);
+  m23 = ((w & 0x800000u) >> 8) | (w & 0x80000000u);
+}
+
 // Wave-wide (64 lanes) reductions.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -75,24 +75,32 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void rq_pow2_kernel(
       }
 
   // Sign masks for the pieces this lane loads: piece (m, s, h) covers
-  // elements base + 0..3 with base = 4 c16 + 64 g + 256 h + 512 s + 1024 m.
+  // elements base + 0..3 with base = 4 c16 + 64 g + 256 h + 512 s + 1024 m;
+  // their four int8 signs are one aligned 32-bit word.
   unsigned smask[MT][2][2][2];
+  if (signs != nullptr) {
+    unsigned sw[MT][2][2];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int base = 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m;
+        for (int h = 0; h < 2; ++h)
+          sw[m][s][h] = *(const unsigned *)(signs + 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m);
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          unsigned mk = 0;
-          if (signs != nullptr) {
-            mk = (signs[base + 2 * d] < 0 ? 0x8000u : 0u) | (signs[base + 2 * d + 1] < 0 ? 0x80000000u : 0u);
-          }
-          smask[m][s][h][d] = mk;
-        }
-      }
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sign_masks4(sw[m][s][h], smask[m][s][h][0], smask[m][s][h][1]);
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) smask[m][s][h][0] = smask[m][s][h][1] = 0u;
+  }
 
   const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerBlock;

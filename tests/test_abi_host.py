@@ -69,6 +69,7 @@ MIS = 0x10001
     (dict(r=rot(n=4096, had=4096, m=1, dense=A16)), qr.QR_EINVAL),
     (dict(r=rot(n=3, had=1, m=3, dense=A16)), qr.QR_ESHAPE),
     (dict(r=None), qr.QR_EINVAL),
+    (dict(r=rot(signs=MIS)), qr.QR_EALIGN),
 ])
 def test_rotate_quant_rejects(args, expect):
     lib = qr.library()
@@ -122,11 +123,12 @@ def test_gemm_i32_rejects():
     (dict(kv=MIS), qr.QR_EALIGN),
     (dict(kv=None), qr.QR_EINVAL),
     (dict(zeros=None), qr.QR_EINVAL),
+    (dict(signs=MIS), qr.QR_EALIGN),
 ])
 def test_kv_rejects(args, expect):
     lib = qr.library()
     st = lib.qr_kv_quant(args.get("kv", A16), args.get("T", 4), 32, args.get("D", 128), args.get("ld", 4096),
-                         None, A16, A16, args.get("zeros", A16), None)
+                         args.get("signs", None), A16, A16, args.get("zeros", A16), None)
     assert st == expect
 
 
