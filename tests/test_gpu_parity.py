@@ -151,6 +151,16 @@ def test_rq_kron_small_dense(qr):
         check_rq(qr, x, had_n * m, had_n, dense=o, signs=signs)
 
 
+@pytest.mark.parametrize("m,rows", [(172, 5), (176, 64), (8, 33), (100, 130), (4, 3)])
+def test_rq_kron_fast_path(qr, m, rows):
+    """64 x m Kronecker rotations without signs (the MFMA Kronecker kernel)."""
+    o = np.linalg.qr(np.random.default_rng(m).standard_normal((m, m)))[0].astype(np.float32)
+    x = W.make_random_rows(rows, 64 * m, seed=m + rows, scale=2.0)
+    x[:, 3] *= 50
+    check_rq(qr, x, 64 * m, 64, dense=o)
+    check_rq(qr, x, 64 * m, 64, dense=o, ld=64 * m + 24)
+
+
 def test_rq_zero_rows_noop(qr):
     rot = qr.Rotation.hadamard(4096)
     x = torch.zeros((0, 4096), dtype=torch.float16, device="cuda")
