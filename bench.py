@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step, time each kernel at every config's shape (one JSON line each)")
     ap.add_argument("--only", default="", help="with --suite: comma-separated case names to run")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="read rocprofv3 FETCH_SIZE / WRITE_SIZE runs of `bench.py --copy-calib MIB` and write "
+                         "profiles/traffic.json (HBM bytes per launch of the GEMM, copy-calibrated)")
+    ap.add_argument("--calib-mib", type=int, default=1024, help="size of the copy used with --ingest-pmc")
     return ap.parse_args()
 
 
@@ -111,6 +115,58 @@ def cpu_baseline(cfg, rows):
             "sample": f"{rows} of {cfg.M} token rows: fp64 explicit-matrix rotation, RTN, int64 GEMM against "
                       f"all {cfg.N} channels (column blocks over {threads} threads), fp64 dequant, KV quant of "
                       f"the sampled rows' K/V; weight prep untimed"}
+
+
+GEMM_SOURCES = ["rotation_bit_quantized_amd/csrc/gemm_prefill.hip", "rotation_bit_quantized_amd/csrc/qr_common.h"]
+
+
+def ingest_pmc(fetch_dir, write_dir, calib_mib):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the prefill GEMM
+    and of the calibration copy; scale the GEMM's by known/measured of the
+    copy (a copy of B bytes reads B and writes B)."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] == counter:
+                    key = (row["Dispatch_Id"], row["Kernel_Name"])
+                    vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+        return vals
+
+    def gemm_avg(vals):
+        v = [x for (d, k), x in vals.items() if "gemm_prefill_kernel" in k]
+        if not v:
+            raise SystemExit("no GEMM dispatches in the counter data")
+        return sum(v) / len(v), [k for (d, k) in vals if "gemm_prefill_kernel" in k][0]
+
+    def copy_max(vals):
+        v = [x for (d, k), x in vals.items() if "copy" in k.lower()]
+        if not v:
+            raise SystemExit("no copy dispatch in the counter data")
+        return max(v)
+
+    fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+    g_fetch, gname = gemm_avg(fetch)
+    g_write, _ = gemm_avg(write)
+    known_kib = calib_mib * 1024.0
+    f_scale = known_kib / copy_max(fetch)
+    w_scale = known_kib / copy_max(write)
+    import re
+    m = re.search(r"gemm_prefill_kernel<[^>]*>", gname)
+    rec = {"int4_gemm_c2": {
+        "kernel": m.group(0) if m else gname[:80], "source_hash": source_hash(GEMM_SOURCES),
+        "fetch_bytes": round(g_fetch * 1024 * f_scale), "write_bytes": round(g_write * 1024 * w_scale),
+        "calibration": {"copy": f"device copy of {calib_mib} MiB (largest copy dispatch)",
+                        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                        "raw_fetch_kib": round(g_fetch, 1), "raw_write_kib": round(g_write, 1)},
+        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 bench.py "
+                   f"--steps 3 --warmup 1 --no-cpu --copy-calib {calib_mib}"}}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(rec))
 
 
 def time_launches(fn, n, warm=3):
@@ -218,6 +274,9 @@ def suite(args):
 
 def main():
     args = parse()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.calib_mib)
+        return
     if args.suite:
         import torch
         import rotation_bit_quantized_amd as qr
@@ -315,9 +374,7 @@ def main():
     rq_bytes = M * K * 2 + M * K // 2 + M * 4
     kv_bytes = 2 * (M * H * 128 * 2 + M * H * 64 + M * H * 5)
     gemm_bytes = M * K // 2 + N * K // 2 + M * 4 + N * 4 + M * N * 2
-    traffic = load_traffic("int4_gemm_c2",
-                           ["rotation_bit_quantized_amd/csrc/gemm_prefill.hip",
-                            "rotation_bit_quantized_amd/csrc/qr_common.h"], gemm_bytes)
+    traffic = load_traffic("int4_gemm_c2", GEMM_SOURCES, gemm_bytes)
 
     out = {
         "metric": "rotate+quant+int4 GEMM TOPS and GB/s at 7B/70B layer shapes; % of roofline",
