@@ -2,8 +2,8 @@
 //
 // Method: QuaRot abstract (all matrix multiplications in 4 bits);
 // dequantizing epilogue y = acc * s_x * s_w per output channel, or the sum
-// over K-groups of 128 of acc_g * s_x[g] * s_w[g] (QuaRot summary, "Key
-// points": group size 128).
+// over K-groups of acc_g * s_x[g] * s_w[g] (QuaRot summary, "Key points":
+// group size 128).
 //
 // CDNA4 has no 4-bit integer MFMA, so codes are widened to int8 in
 // registers right after they are read from LDS, in "high-nibble" form:
@@ -15,32 +15,39 @@
 // The 1/256 is an exact power of two folded into the epilogue (or a shift
 // for the int32 output).
 //
-// Data movement: 256 threads (2 x 2 waves), two blocks per CU, block tile
-// BM x BN, K-tile 128 codes = 64 bytes per row.  K-tiles travel from global
-// memory straight into LDS with global_load_lds_dwordx4 (no VGPR staging),
-// through STAGES LDS buffers: while the waves multiply K-tile kt, the loads
-// of K-tiles kt+1 .. kt+STAGES-1 are in flight.  A wave waits (vmcnt) only
-// for its own pieces of tile kt, then one s_barrier makes everyone's pieces
-// visible and also certifies that the buffer about to be refilled has been
-// consumed.  A DMA wave instruction fills 1 KB of LDS contiguously (lane i
-// -> bytes 16i..16i+15), i.e. 16 rows x four 16-byte pieces; each lane
-// fetches the global piece (slot ^ swz(row)) so that the fragment reads -
-// 16 consecutive rows at one piece - hit 16 distinct bank groups.
+// Data movement: block tile BM x BN, K-tile 256 codes = 128 bytes per row,
+// i.e. one whole 128-byte cache line per row and K-tile (half-line rows
+// halve the L2 -> LDS fill rate of a CU).  K-tiles travel from global memory
+// straight into LDS with global_load_lds_dwordx4 (no VGPR staging) through
+// STAGES LDS buffers.  A DMA wave instruction fills 1 KB of LDS contiguously
+// (lane i -> bytes 16i..16i+15), i.e. 8 rows x eight 16-byte pieces; each
+// lane fetches the global piece swz(row, slot), so that the fragment reads
+// (16 consecutive rows at one piece) hit 16 distinct bank groups.
 //
-// Compute: each wave owns a (BM/2) x (BN/2) sub-tile of 32x32 fragments (up
-// to 128 x 128 = 256 accumulators), so each widened operand feeds FN (or FM)
-// MFMAs; one 16-byte LDS read per fragment row feeds two
-// v_mfma_i32_32x32x32_i8 k-steps, and the second read of a K-tile is issued
-// before the first is widened.  The host picks BN so that the tile count
-// fills the CU slots evenly (128 x 192 tiles for 2048 x 12288).
+// The K loop is software-pipelined over 64-code chunks (one 16-byte LDS read
+// per fragment row and lane, two MFMA k-steps after widening): the read of
+// chunk c+1 is in flight while chunk c is multiplied.  Once per K-tile, a
+// wave waits (vmcnt, its own DMA pieces only) for the next tile and meets
+// the other waves at one s_barrier, which makes that tile visible and
+// certifies that every wave holds the current tile's last chunk in
+// registers, so the current buffer is refilled at once.  When K is an odd
+// multiple of 128 the last K-tile carries 128 codes (two chunks); its DMA
+// lanes for the missing half re-read the present half.
+//
+// Compute: each wave owns a WM x WN sub-tile of 32x32 fragments of
+// v_mfma_i32_32x32x32_i8, so each widened operand feeds FN (or FM) MFMAs.
+// The host picks the block shape whose tile count fills the CU slots best.
 #include "qr_common.h"
 #include "qr_launch.h"
+
+#include <type_traits>
 
 namespace qr {
 namespace {
 
-constexpr int kBK = 128;        // codes per K-tile
-constexpr int kRowBytes = 64;   // bytes per row per K-tile
+constexpr int kBK = 256;         // codes per K-tile
+constexpr int kRowBytes = 128;   // bytes per row per K-tile
+constexpr int kHalfCodes = 128;  // a group spans whole halves of a K-tile
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -55,8 +62,10 @@ __device__ __forceinline__ void widen(const v4u &w, v4i &op0, v4i &op1) {
   op1[3] = (int)(w[3] & 0xF0F0F0F0u);
 }
 
-// LDS slot of 16-byte piece p (0..3) of tile row r (an involution in p).
-__device__ __forceinline__ int swz(int r, int p) { return p ^ ((r >> 2) & 3); }
+// LDS slot of 16-byte piece p (0..7) of tile row r (an involution in p).
+// Rows are 128 bytes, so rows 2t and 2t+1 share a 256-byte bank window;
+// xoring with t spreads 16 consecutive rows over all 16 slots of the window.
+__device__ __forceinline__ int swz(int r, int p) { return p ^ ((r >> 1) & 7); }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -64,6 +73,9 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// s_waitcnt lgkmcnt(0), vmcnt and expcnt left alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Map the linear block id to a (tile_m, tile_n): consecutive hardware block
 // ids go to different XCDs (round robin over 8), so first regroup them so
@@ -85,26 +97,31 @@ __device__ __forceinline__ void tile_of(int bid, int tm_count, int tn_count, int
   tn = in_band / gm;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GROUPED, bool OUT_I32>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N) > 0 ? 2 : 1) void gemm_prefill_kernel(
+// Blocks of 4 waves run two to a CU, blocks of 8 waves one: two waves per
+// SIMD either way.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GROUPED, bool OUT_I32, bool SHORT_TAIL>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) void gemm_prefill_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ W,
     const float *__restrict__ sw, int M, int N, int K, int group, void *__restrict__ out, int64_t ld_y) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int ROWS = BM + BN;
   constexpr bool SCALES = GROUPED && !OUT_I32;   // group scales travel with the K-tiles
-  constexpr int SCALE_BYTES = SCALES ? (BM + BN) * 4 : 0;
-  constexpr int SCALE_INST = SCALES ? (BM + BN) / 64 : 0;   // 4-byte DMA wave-instructions per stage
-  constexpr int STAGE_BYTES = (BM + BN) * kRowBytes + SCALE_BYTES;
-  static_assert(!SCALES || ((BM + BN) % 64 == 0 && SCALE_INST % NW == 0), "scale DMA split");
+  // one scale set (s_x of the BM rows, then s_w of the BN columns) per K-tile half
+  constexpr int SCALE_BYTES = SCALES ? 2 * ROWS * 4 : 0;
+  constexpr int SCALE_INST = SCALES ? 2 * ROWS / 64 : 0;   // 4-byte DMA wave-instructions per stage
+  constexpr int STAGE_BYTES = ROWS * kRowBytes + SCALE_BYTES;
+  static_assert(!SCALES || (ROWS % 32 == 0 && SCALE_INST % NW == 0), "scale DMA split");
   constexpr int SCALE_LOADS = SCALE_INST / NW;
-  constexpr int TI = (BM + BN) / 16;              // DMA wave-instructions per stage (16 rows each)
+  constexpr int TI = ROWS / 8;                    // DMA wave-instructions per stage (8 rows each)
   constexpr int LOADS = TI / NW;                  // per wave
   static_assert(TI % NW == 0, "tile rows must split evenly over the waves' DMA instructions");
+  static_assert(NW % 2 == 0, "the upper-piece rule below assumes an even wave count");
   constexpr int WAVE_LOADS = LOADS + SCALE_LOADS;  // vmem ops per wave per stage
-  static_assert(WAVE_LOADS * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(STAGES >= 2 && STAGES <= 3, "pipeline depth");
+  static_assert(WAVE_LOADS * (STAGES - 1) < 64, "vmcnt range");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
@@ -120,43 +137,57 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N) > 0
   tile_of(blockIdx.x, tm_count, tn_count, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int64_t kbytes = K / 2;
-  const int KT = K / kBK;
-  const int tiles_per_group = GROUPED ? group / kBK : 1;
+  const int KT = (K + kBK - 1) / kBK;
+  // SHORT_TAIL: K is an odd multiple of 128, the last K-tile holds 128 codes
+  const int halves_per_group = GROUPED ? group / kHalfCodes : 1;
 
   // DMA sources: wave-instruction q of this wave fills tile rows
-  // 16 (NW q + wave) .. +15 (A rows first, then W rows); lane l writes LDS
-  // slot l % 4 of row l / 4 with global piece swz(row, slot).  Rows past the
-  // matrix edge re-read the last row; their results are never stored.
-  const uint8_t *src[LOADS];
+  // 8 (NW q + wave) .. +7 (A rows first, then W rows); lane l writes LDS
+  // slot l % 8 of row l / 8 with global piece swz(row, l % 8).  Rows past
+  // the matrix edge re-read the last row; their results are never stored.
+  // Whether an instruction reads A or W is uniform; the per-lane part is a
+  // 32-bit offset from the block's first row.
+  const uint8_t *a_base = A + (int64_t)m0 * kbytes;
+  const uint8_t *w_base = W + (int64_t)n0 * kbytes;
+  uint32_t src_off[LOADS];
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) {
-    const int trow = 16 * (NW * q + wave) + (lane >> 2);   // 0 .. BM+BN-1
-    const int piece = swz(trow, lane & 3);
-    if (trow < BM) {
-      const int gr = min(m0 + trow, M - 1);
-      src[q] = A + (int64_t)gr * kbytes + piece * 16;
-    } else {
-      const int gr = min(n0 + trow - BM, N - 1);
-      src[q] = W + (int64_t)gr * kbytes + piece * 16;
-    }
+    const int trow = 8 * (NW * q + wave) + (lane >> 3);   // 0 .. ROWS-1
+    const int piece = swz(trow, lane & 7);
+    const int rel = trow < BM ? min(trow, M - 1 - m0) : min(trow - BM, N - 1 - n0);
+    src_off[q] = (uint32_t)rel * (uint32_t)kbytes + (uint32_t)(piece * 16);
   }
-  auto issue = [&](int kt, int stage) {
+  // Whether this lane's global piece lies in the upper half of the row
+  // (piece >= 4): with trow = 8 X + (lane >> 3), (trow >> 1) & 7 equals
+  // 4 (X & 1) + (lane >> 4), and X = NW q + wave has the parity of wave, so
+  // bit 2 of the piece is bit 2 of lane xor bit 0 of wave, for every q.
+  const int upper_piece = ((lane >> 2) ^ wave) & 1;
+  const uint32_t tail_back = upper_piece ? 64u : 0u;   // a short last tile re-reads the lower half
+
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    const bool short_tile = SHORT_TAIL && kt == KT - 1;
+    const uint8_t *ak = a_base + kt * kRowBytes;
+    const uint8_t *wk = w_base + kt * kRowBytes;
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q)
-      __builtin_amdgcn_global_load_lds((const void *)(src[q] + kt * kRowBytes),
+    for (int q = 0; q < LOADS; ++q) {
+      const bool in_a = 8 * (NW * q + wave) < BM;
+      const uint32_t o = short_tile ? src_off[q] - tail_back : src_off[q];
+      __builtin_amdgcn_global_load_lds((const void *)((in_a ? ak : wk) + o),
                                        (lds_void *)(smem + stage * STAGE_BYTES + (NW * q + wave) * 1024), 16,
                                        0, 0);
+    }
     if constexpr (SCALES) {
-      // the group's scales: s_x of the BM tile rows, then s_w of the BN tile columns
       const int G = K / group;
-      const int gidx = kt * kBK / group;
 #pragma unroll
       for (int q = 0; q < SCALE_LOADS; ++q) {
-        const int e = 64 * (NW * q + wave) + lane;
-        const float *p = e < BM ? sa + (int64_t)min(m0 + e, M - 1) * G + gidx
-                                : sw + (int64_t)min(n0 + e - BM, N - 1) * G + gidx;
+        const int e = 64 * (NW * q + wave) + lane;   // 0 .. 2 ROWS - 1
+        const int h = e >= ROWS;
+        const int ee = e - h * ROWS;
+        const int gidx = min((kt * kBK + h * kHalfCodes) / group, G - 1);
+        const float *p = ee < BM ? sa + (int64_t)min(m0 + ee, M - 1) * G + gidx
+                                 : sw + (int64_t)min(n0 + ee - BM, N - 1) * G + gidx;
         __builtin_amdgcn_global_load_lds((const void *)p,
-                                         (lds_void *)(smem + stage * STAGE_BYTES + (BM + BN) * kRowBytes +
+                                         (lds_void *)(smem + stage * STAGE_BYTES + ROWS * kRowBytes +
                                                       256 * (NW * q + wave)),
                                          4, 0, 0);
       }
@@ -180,97 +211,216 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N) > 0
   const int lcol = lane & 31;
   const int ra = wm * WM + (lane & 31);            // tile row of this lane in A fragment 0
   const int rb = BM + wn * WN + (lane & 31);       // tile row of this lane in W fragment 0
-  const int half = lane >> 5;                      // which 16-byte half of a 32-byte chunk
+  const int half = lane >> 5;                      // which 16-byte piece of a 32-byte chunk
 
+  // Chunk pipeline registers: the raw codes of two chunks (LDS -> VGPR, one
+  // read in flight while the other is widened) and the widened operands of
+  // two chunks (the one being multiplied, the next one being widened).
+  v4u rawA[2][FM], rawB[2][FN];        // [buffer][fragment]
+  v4i opA[2][FM][2], opB[2][FN][2];   // [buffer][fragment][k-step]
+
+  // Raw fragment reads of chunk `kk` (codes 64 kk .. 64 kk + 63) of the
+  // K-tile in `st` into raw buffer `rb_`.
+  auto read_raw = [&](const uint8_t *st, int kk, int rbuf) __attribute__((always_inline)) {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s, s);
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt % STAGES;
-    // wait for this wave's pieces of tile kt; later tiles may stay in flight
-    // (kt is uniform, so these are scalar branches)
-    const int ahead = min(STAGES - 2, KT - 1 - kt);
-    if (ahead >= 2) wait_vm<2 * WAVE_LOADS>();
-    else if (ahead == 1) wait_vm<WAVE_LOADS>();
+    for (int i = 0; i < FM; ++i) {
+      const int r = ra + 32 * i;
+      rawA[rbuf][i] = *(const v4u *)(st + r * kRowBytes + swz(r, 2 * kk + half) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = rb + 32 * j;
+      rawB[rbuf][j] = *(const v4u *)(st + r * kRowBytes + swz(r, 2 * kk + half) * 16);
+    }
+  };
+  auto widen_into = [&](int rbuf, int obuf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) widen(rawA[rbuf][i], opA[obuf][i][0], opA[obuf][i][1]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) widen(rawB[rbuf][j], opB[obuf][j][0], opB[obuf][j][1]);
+  };
+  // The MFMAs of the chunk in operand buffer `obuf` (two k-steps); with
+  // ZERO the first k-step starts from zero (a new K-group).
+  auto mma_chunk = [&](int obuf, auto zero_c) __attribute__((always_inline)) {
+    constexpr bool ZERO = decltype(zero_c)::value;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (ZERO && ks == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(opA[obuf][i][ks], opB[obuf][j][ks], v16i{}, 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(opA[obuf][i][ks], opB[obuf][j][ks], acc[i][j], 0, 0, 0);
+        }
+  };
+  // Multiply operand buffer `obuf` and, interleaved with it, widen raw
+  // buffer `rbuf` into the other operand buffer (when `do_widen`).
+  auto compute = [&](int obuf, int rbuf, bool zero, auto widen_c) __attribute__((always_inline)) {
+    constexpr bool DO_WIDEN = decltype(widen_c)::value;
+    if (GROUPED && zero) {
+      mma_chunk(obuf, std::true_type{});
+      if constexpr (DO_WIDEN) widen_into(rbuf, 1 - obuf);
+    } else {
+      mma_chunk(obuf, std::false_type{});
+      if constexpr (DO_WIDEN) widen_into(rbuf, 1 - obuf);
+    }
+  };
+  // Wait until this wave's DMA pieces of a tile have landed; `issued_after`
+  // tiles issued later may stay in flight (scalar branches: uniform).
+  auto wait_tile = [&](int issued_after) __attribute__((always_inline)) {
+    if (issued_after >= 2) wait_vm<2 * WAVE_LOADS>();
+    else if (issued_after == 1) wait_vm<WAVE_LOADS>();
     else wait_vm<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+  };
 
-    const uint8_t *st = smem + cur * STAGE_BYTES;
-    const bool fresh = GROUPED && (kt % tiles_per_group == 0);
-    v4u araw[2][FM], braw[2][FN];
+  // Group scales of K-tile half h, from the stage at `st`, into registers
+  // (s_w pre-multiplied by the 1/256 of the widening).
+  v4f gsa[SCALES ? FM : 1][4];
+  float gsw[SCALES ? FN : 1];
+  auto read_scales = [&](const uint8_t *st, int h) __attribute__((always_inline)) {
+    const float *sc = (const float *)(st + ROWS * kRowBytes) + h * ROWS;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int j = 0; j < FN; ++j) gsw[j] = sc[BM + wn * WN + j * 32 + lcol] * (1.0f / 256.0f);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = ra + 32 * i;
-        araw[kk][i] = *(const v4u *)(st + r * kRowBytes + swz(r, 2 * kk + half) * 16);
-      }
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = rb + 32 * j;
-        braw[kk][j] = *(const v4u *)(st + r * kRowBytes + swz(r, 2 * kk + half) * 16);
-      }
-    }
+      for (int r4 = 0; r4 < 4; ++r4) gsa[i][r4] = *(const v4f *)(sc + wm * WM + i * 32 + 8 * r4 + lrow);
+  };
+  // A K-group ends with half h of K-tile kt: fold or store its partial sums.
+  auto group_end = [&](int kt, int h) __attribute__((always_inline)) {
+    if constexpr (OUT_I32) {
+      const int gidx = (kt * kBK + h * kHalfCodes) / group;
+      int32_t *o = (int32_t *)out + (int64_t)gidx * M * N;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      v4i aop[FM][2], bop[FN][2];
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) widen(araw[kk][i], aop[i][0], aop[i][1]);
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + wn * WN + j * 32 + lcol;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) widen(braw[kk][j], bop[j][0], bop[j][1]);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            if (GROUPED && fresh && kk == 0 && ks == 0)
-              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[i][ks], bop[j][ks], v16i{}, 0, 0, 0);
-            else
-              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[i][ks], bop[j][ks], acc[i][j], 0, 0, 0);
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
+            if (row < M && col < N) o[(int64_t)row * N + col] = acc[i][j][r] >> 8;
           }
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              facc[i][j][4 * r4 + r] =
+                  __builtin_fmaf((float)acc[i][j][4 * r4 + r], gsa[i][r4][r] * gsw[j], facc[i][j][4 * r4 + r]);
     }
+  };
+  // Chunk boundary: the raw read issued a chunk ago must have landed (the
+  // wait is fenced so that nothing is scheduled across it).
+  auto chunk_fence = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-    if constexpr (GROUPED) {
-      if ((kt + 1) % tiles_per_group == 0) {
-        const int gidx = kt / tiles_per_group;
-        const int G = K / group;
-        if constexpr (OUT_I32) {
-          int32_t *o = (int32_t *)out + (int64_t)gidx * M * N;
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-              const int col = n0 + wn * WN + j * 32 + lcol;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
-                if (row < M && col < N) o[(int64_t)row * N + col] = acc[i][j][r] >> 8;
-              }
-            }
-        } else {
-          const float *sc = (const float *)(st + (BM + BN) * kRowBytes);
-          float gsw[FN];
-#pragma unroll
-          for (int j = 0; j < FN; ++j) gsw[j] = sc[BM + wn * WN + j * 32 + lcol] * (1.0f / 256.0f);
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const v4f s4 = *(const v4f *)(sc + wm * WM + i * 32 + 8 * r4 + lrow);
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                  facc[i][j][4 * r4 + r] =
-                      __builtin_fmaf((float)acc[i][j][4 * r4 + r], s4[r] * gsw[j], facc[i][j][4 * r4 + r]);
-            }
+  // One K-tile.  On entry chunk 0 is widened in operand buffer 0 and the
+  // raw read of chunk 1 (raw buffer 1) is in flight.  Each chunk: wait for
+  // the raw read issued a chunk ago, issue the raw read of the chunk after
+  // next into the free raw buffer, then multiply while widening the next
+  // chunk into the other operand buffer.  Reads are pinned in place (the
+  // scheduler would otherwise sink them next to their use).  At chunk 2 the
+  // waves meet at the tile barrier: every wave then holds this tile's last
+  // raw chunk, so its LDS buffer is refilled at once, and the next tile
+  // (waited for just before) becomes readable.  Mode kNext: a tile followed
+  // by another; kLastFull: the last tile, 256 codes; kLastShort: the last
+  // tile, 128 codes.
+  constexpr int kNext = 0, kLastFull = 1, kLastShort = 2;
+  auto tile = [&](int kt, auto mode_c) __attribute__((always_inline)) {
+    constexpr int mode = decltype(mode_c)::value;
+    const uint8_t *st = smem + (kt % STAGES) * STAGE_BYTES;
+    const uint8_t *nst = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
+    // groups are whole halves: one can start with half 0 or half 1 and end with either
+    const bool start0 = GROUPED && ((2 * kt) % halves_per_group == 0);
+    const bool start1 = GROUPED && ((2 * kt + 1) % halves_per_group == 0);
+    const bool end1 = GROUPED && ((2 * kt + 2) % halves_per_group == 0);
+
+    if constexpr (mode == kLastShort) {
+      chunk_fence();
+      compute(0, 1, start0, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1, 0, false, std::false_type{});
+      if constexpr (GROUPED) {   // the last half ends the last group
+        if constexpr (SCALES) read_scales(st, 0);
+        group_end(kt, 0);
+      }
+      return;
+    } else {
+      // chunk 0
+      chunk_fence();
+      read_raw(st, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0, 1, start0, std::true_type{});
+      // chunk 1
+      chunk_fence();
+      read_raw(st, 3, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1, 0, false, std::true_type{});
+      if constexpr (GROUPED) {
+        if (start1) {   // half 0 closes a group
+          if constexpr (SCALES) read_scales(st, 0);
+          group_end(kt, 0);
         }
       }
+      // chunk 2
+      chunk_fence();
+      if constexpr (SCALES) {
+        // this stage is refilled after the barrier below: take the scales first
+        if (end1) read_scales(st, 1);
+      }
+      if constexpr (mode == kNext) {
+        wait_tile(min(STAGES - 2, KT - 2 - kt));
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        if (kt + STAGES < KT) issue(kt + STAGES, kt % STAGES);
+        read_raw(nst, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0, 1, start1, std::true_type{});
+      // chunk 3
+      if constexpr (mode == kNext) {
+        chunk_fence();
+        read_raw(nst, 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1, 0, false, std::true_type{});
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1, 0, false, std::false_type{});
+      }
+      if constexpr (GROUPED) {
+        if (end1) group_end(kt, 1);
+      }
     }
-  }
+  };
+
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s)
+    if (s < KT) issue(s, s);
+  wait_tile(min(STAGES - 1, KT - 1));
+  __builtin_amdgcn_s_barrier();
+  read_raw(smem, 0, 0);
+  wait_lgkm0();
+  widen_into(0, 0);
+  read_raw(smem, 1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int kt = 0; kt + 1 < KT; ++kt) tile(kt, std::integral_constant<int, kNext>{});
+  if constexpr (SHORT_TAIL)
+    tile(KT - 1, std::integral_constant<int, kLastShort>{});
+  else
+    tile(KT - 1, std::integral_constant<int, kLastFull>{});
+  __builtin_amdgcn_sched_barrier(0);   // keep the epilogue out of the last MFMAs
 
   // ---- epilogue
   if constexpr (OUT_I32 && !GROUPED) {
@@ -287,34 +437,74 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N) > 0
         }
       }
   } else if constexpr (!OUT_I32) {
+    // fp16 output, staged through LDS: each wave writes its WM x WN tile
+    // row-major into a private region of the (now idle) stage buffers, then
+    // stores whole 16-byte row pieces (2-byte stores straight from the
+    // fragment layout, one column per lane, would take 8x the store
+    // instructions and stall the CU's two blocks together).
+    constexpr int PITCH = WN * 2 + 16;   // bytes per LDS row; the pad spreads the two half-waves' banks
+    static_assert(NW * WM * PITCH <= STAGES * STAGE_BYTES, "epilogue staging must fit in the stage buffers");
+    static_assert((WM * (WN / 8)) % 64 == 0, "whole wave passes over the output pieces");
     unsigned short *y = (unsigned short *)out;
-    float swv[FN];
+    // Output scales: every load issued at once from clamped (always valid)
+    // indices, before the barrier, so that one memory latency covers them;
+    // rows or columns past the edge are never stored.
+    float swv[FN], sav[GROUPED ? 1 : FM][16];
     if constexpr (!GROUPED) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * WN + j * 32 + lcol;
-        swv[j] = col < N ? sw[col] * (1.0f / 256.0f) : 0.f;
-      }
+      for (int j = 0; j < FN; ++j) swv[j] = sw[min(n0 + wn * WN + j * 32 + lcol, N - 1)] * (1.0f / 256.0f);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sav[i][r] = sa[min(m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3), M - 1)];
     }
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();   // every wave is done reading the stage buffers
+    uint8_t *ot = smem + wave * WM * PITCH;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
-        if (row >= M) continue;
-        const float sav = GROUPED ? 0.f : sa[row];
+        const int trow = i * 32 + 8 * (r >> 2) + lrow + (r & 3);   // row within the wave tile
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WN + j * 32 + lcol;
-          if (col >= N) continue;
           float val;
           if constexpr (GROUPED)
             val = facc[i][j][r];
           else
-            val = (float)acc[i][j][r] * (sav * swv[j]);
-          y[(int64_t)row * ld_y + col] = float_to_half_bits(val);
+            val = (float)acc[i][j][r] * (sav[i][r] * swv[j]);
+          *(unsigned short *)(ot + trow * PITCH + (j * 32 + lcol) * 2) = float_to_half_bits(val);
         }
       }
+    // the wave reads back only what it wrote itself: LDS operations of one
+    // wave complete in order, no barrier needed
+    const bool vec_ok = ((uintptr_t)y % 16 == 0) && (ld_y % 8 == 0);
+    constexpr int PIECES = WN / 8;   // 16-byte pieces per row
+    constexpr int PASSES = WM * PIECES / 64;
+    v4u pv[PASSES];   // all reads first, then the (edge-guarded) stores
+#pragma unroll
+    for (int it = 0; it < PASSES; ++it) {
+      const int p = it * 64 + lane;
+      pv[it] = *(const v4u *)(ot + (p / PIECES) * PITCH + (p % PIECES) * 16);
+    }
+#pragma unroll
+    for (int it = 0; it < PASSES; ++it) {
+      const int p = it * 64 + lane;
+      const int trow = p / PIECES, cp = p % PIECES;
+      const int row = m0 + wm * WM + trow;
+      const int col = n0 + wn * WN + cp * 8;
+      const v4u v = pv[it];
+      if (row < M) {
+        unsigned short *dst = y + (int64_t)row * ld_y + col;
+        if (vec_ok && col + 8 <= N) {
+          *(v4u *)dst = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < N) dst[e] = (unsigned short)(v[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
   }
 }
 
@@ -324,12 +514,18 @@ hipError_t launch_cfg(const uint8_t *a, const float *sa, const uint8_t *w, const
                       hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
-  if (out_i32)
-    gemm_prefill_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, GROUPED, true><<<grid, block, 0, stream>>>(
-        a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y);
-  else
-    gemm_prefill_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, GROUPED, false><<<grid, block, 0, stream>>>(
-        a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y);
+  const bool short_tail = K % kBK != 0;
+#define QR_GEMM_LAUNCH(I32, TAIL)                                                                \
+  gemm_prefill_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, GROUPED, I32, TAIL><<<grid, block, 0, stream>>>( \
+      a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y)
+  if (out_i32) {
+    if (short_tail) QR_GEMM_LAUNCH(true, true);
+    else QR_GEMM_LAUNCH(true, false);
+  } else {
+    if (short_tail) QR_GEMM_LAUNCH(false, true);
+    else QR_GEMM_LAUNCH(false, false);
+  }
+#undef QR_GEMM_LAUNCH
   return hipGetLastError();
 }
 
@@ -338,29 +534,24 @@ hipError_t launch_cfg(const uint8_t *a, const float *sa, const uint8_t *w, const
 hipError_t launch_gemm_prefill(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,
                                int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
                                bool out_i32, hipStream_t stream) {
-  // 4-wave blocks sized so that two fit on a CU (LDS and registers): the two
-  // waves sharing a SIMD then come from independent blocks whose barriers
-  // drift out of phase, and one multiplies while the other waits.
   if (group != 0)
-    return launch_cfg<128, 128, 2, 2, 3, true>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+    return launch_cfg<128, 128, 2, 2, 2, true>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int64_t slots = 2 * (int64_t)cus;
   // fraction of the busy slot-rounds doing useful work, times the fraction of
   // the tile area inside the matrix, times a mild preference for bigger tiles
-  auto score = [&](int64_t bm, int64_t bn, double size_pref) {
+  auto score = [&](int64_t bm, int64_t bn, int64_t per_cu, double size_pref) __attribute__((always_inline)) {
+    const int64_t slots = per_cu * cus;
     const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
     const int64_t tiles = tm * tn;
     const int64_t rounds = (tiles + slots - 1) / slots;
     return (double)tiles / (double)(rounds * slots) * (double)(M * N) / (double)(tm * bm * tn * bn) * size_pref;
   };
-  const double s_256x128 = score(256, 128, 1.0), s_128x192 = score(128, 192, 0.99), s_128x128 = score(128, 128, 0.9);
-  if (s_256x128 >= s_128x192 && s_256x128 >= s_128x128)
-    return launch_cfg<256, 128, 2, 2, 3, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+  const double s_128x192 = score(128, 192, 2, 1.0), s_128x128 = score(128, 128, 2, 0.9);
   if (s_128x192 >= s_128x128)
-    return launch_cfg<128, 192, 2, 2, 3, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
-  return launch_cfg<128, 128, 2, 2, 3, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+    return launch_cfg<128, 192, 2, 2, 2, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+  return launch_cfg<128, 128, 2, 2, 2, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
 }
 
 }  // namespace qr

@@ -201,6 +201,11 @@ def test_weight_prep_on_gpu_matches_oracle(qr, cfg, ncols):
     (1, 33, 512, 0),          # single token
     (48, 96, 1024, 128),      # decode, group-wise
     (65, 70, 256, 0),         # smallest prefill M
+    (200, 300, 384, 0),       # K an odd multiple of 128: a half K-tile at the end
+    (129, 64, 128, 0),        # only that half tile
+    (192, 256, 640, 128),     # group-wise with the half tile
+    (150, 160, 1152, 384),    # groups that straddle K-tiles, half tile at the end
+    (100, 96, 1536, 768),     # groups of three K-tiles
 ])
 def test_gemm_i32_exact(qr, M, N, K, group):
     qa = W.make_random_codes(M, K, seed=M + K)
@@ -224,7 +229,8 @@ def test_gemm_i32_exact_on_oracle_codes_c1(qr):
 # ------------------------------------------------------------------ fp16 epilogue
 
 @pytest.mark.parametrize("M,N,K,group", [(64, 512, 512, 0), (320, 640, 4096, 0), (257, 130, 1024, 128),
-                                         (40, 300, 1024, 128), (130, 96, 11008, 0)])
+                                         (40, 300, 1024, 128), (130, 96, 11008, 0), (130, 96, 384, 0),
+                                         (257, 130, 640, 128), (150, 160, 1152, 384)])
 def test_gemm_epilogue_on_given_codes(qr, M, N, K, group):
     rng = np.random.default_rng(M * N)
     qa = W.make_random_codes(M, K, seed=M)
@@ -251,6 +257,27 @@ def test_gemm_padded_output(qr):
     yb = host(ybuf)
     assert np.all(yb[:, 70:] == 7.0)          # padding untouched
     check_output(yb[:, :70], O.dequantize_output(O.int_gemm(qa, qw), sa, sw))
+
+
+@pytest.mark.parametrize("M,N,K,group", [(130, 70, 512, 0), (200, 200, 640, 128), (300, 389, 1024, 0)])
+def test_gemm_unaligned_output(qr, M, N, K, group):
+    """y 2-byte aligned only and a row pitch that is not a multiple of 8:
+    the epilogue's element-wise store path."""
+    qa = W.make_random_codes(M, K, seed=3 * M)
+    qw = W.make_random_codes(N, K, seed=5 * N)
+    G = 1 if group == 0 else K // group
+    rng = np.random.default_rng(K)
+    sa = (rng.random((M, G)) * 0.1 + 0.01).astype(np.float32)
+    sw = (rng.random((N, G)) * 0.01 + 0.001).astype(np.float32)
+    if group == 0:
+        sa, sw = sa[:, 0].copy(), sw[:, 0].copy()
+    ybuf = torch.full((M, N + 7), 3.0, dtype=torch.float16, device="cuda")
+    y = ybuf[:, 1:N + 1]
+    assert y.data_ptr() % 16 != 0 and y.stride(0) % 8 != 0
+    qr.int4_gemm(dev(O.pack_int4(qa)), dev(sa), dev(O.pack_int4(qw)), dev(sw), group, y=y)
+    yb = host(ybuf)
+    assert np.all(yb[:, 0] == 3.0) and np.all(yb[:, N + 1:] == 3.0)   # outside the view untouched
+    check_output(yb[:, 1:N + 1], O.dequantize_output(O.int_gemm(qa, qw, group), sa, sw, group))
 
 
 # ------------------------------------------------------------------ whole layer, GPU path end to end
