@@ -74,6 +74,13 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// A compile-time range [LO, HI) of DMA wave-instructions.
+template <int LO, int HI>
+struct DmaRange {
+  static constexpr int lo = LO, hi = HI;
+};
+using NoDma = DmaRange<0, 0>;
+
 // s_waitcnt lgkmcnt(0), vmcnt and expcnt left alone.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -164,34 +171,37 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
   const int upper_piece = ((lane >> 2) ^ wave) & 1;
   const uint32_t tail_back = upper_piece ? 64u : 0u;   // a short last tile re-reads the lower half
 
-  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+  // DMA wave-instruction q of K-tile kt into `stage` (the group scales go
+  // with the last one).
+  auto issue_q = [&](int kt, int stage, int q) __attribute__((always_inline)) {
     const bool short_tile = SHORT_TAIL && kt == KT - 1;
-    const uint8_t *ak = a_base + kt * kRowBytes;
-    const uint8_t *wk = w_base + kt * kRowBytes;
-#pragma unroll
-    for (int q = 0; q < LOADS; ++q) {
-      const bool in_a = 8 * (NW * q + wave) < BM;
-      const uint32_t o = short_tile ? src_off[q] - tail_back : src_off[q];
-      __builtin_amdgcn_global_load_lds((const void *)((in_a ? ak : wk) + o),
-                                       (lds_void *)(smem + stage * STAGE_BYTES + (NW * q + wave) * 1024), 16,
-                                       0, 0);
-    }
+    const bool in_a = 8 * (NW * q + wave) < BM;
+    const uint8_t *base = (in_a ? a_base : w_base) + kt * kRowBytes;
+    const uint32_t o = short_tile ? src_off[q] - tail_back : src_off[q];
+    __builtin_amdgcn_global_load_lds((const void *)(base + o),
+                                     (lds_void *)(smem + stage * STAGE_BYTES + (NW * q + wave) * 1024), 16, 0, 0);
     if constexpr (SCALES) {
-      const int G = K / group;
+      if (q == LOADS - 1) {
+        const int G = K / group;
 #pragma unroll
-      for (int q = 0; q < SCALE_LOADS; ++q) {
-        const int e = 64 * (NW * q + wave) + lane;   // 0 .. 2 ROWS - 1
-        const int h = e >= ROWS;
-        const int ee = e - h * ROWS;
-        const int gidx = min((kt * kBK + h * kHalfCodes) / group, G - 1);
-        const float *p = ee < BM ? sa + (int64_t)min(m0 + ee, M - 1) * G + gidx
-                                 : sw + (int64_t)min(n0 + ee - BM, N - 1) * G + gidx;
-        __builtin_amdgcn_global_load_lds((const void *)p,
-                                         (lds_void *)(smem + stage * STAGE_BYTES + ROWS * kRowBytes +
-                                                      256 * (NW * q + wave)),
-                                         4, 0, 0);
+        for (int qs = 0; qs < SCALE_LOADS; ++qs) {
+          const int e = 64 * (NW * qs + wave) + lane;   // 0 .. 2 ROWS - 1
+          const int h = e >= ROWS;
+          const int ee = e - h * ROWS;
+          const int gidx = min((kt * kBK + h * kHalfCodes) / group, G - 1);
+          const float *p = ee < BM ? sa + (int64_t)min(m0 + ee, M - 1) * G + gidx
+                                   : sw + (int64_t)min(n0 + ee - BM, N - 1) * G + gidx;
+          __builtin_amdgcn_global_load_lds((const void *)p,
+                                           (lds_void *)(smem + stage * STAGE_BYTES + ROWS * kRowBytes +
+                                                        256 * (NW * qs + wave)),
+                                           4, 0, 0);
+        }
       }
     }
+  };
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) issue_q(kt, stage, q);
   };
 
   v16i acc[FM][FN];
@@ -240,9 +250,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
     for (int j = 0; j < FN; ++j) widen(rawB[rbuf][j], opB[obuf][j][0], opB[obuf][j][1]);
   };
   // The MFMAs of the chunk in operand buffer `obuf` (two k-steps); with
-  // ZERO the first k-step starts from zero (a new K-group).
-  auto mma_chunk = [&](int obuf, auto zero_c) __attribute__((always_inline)) {
+  // ZERO the first k-step starts from zero (a new K-group).  DMA
+  // instructions [Q_LO, Q_HI) of K-tile dkt (into dstage) are issued one
+  // after each MFMA: issued as a burst, they would hold up the wave at the
+  // memory pipeline while the matrix core idles.
+  auto mma_chunk = [&](int obuf, auto zero_c, auto dma_c, int dkt, int dstage) __attribute__((always_inline)) {
     constexpr bool ZERO = decltype(zero_c)::value;
+    constexpr int Q_LO = decltype(dma_c)::lo, Q_HI = decltype(dma_c)::hi;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -253,18 +267,33 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(opA[obuf][i][ks], opB[obuf][j][ks], v16i{}, 0, 0, 0);
           else
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(opA[obuf][i][ks], opB[obuf][j][ks], acc[i][j], 0, 0, 0);
+          const int idx = (ks * FM + i) * FN + j;
+          if (Q_LO + idx < Q_HI) issue_q(dkt, dstage, Q_LO + idx);
         }
   };
   // Multiply operand buffer `obuf` and, interleaved with it, widen raw
-  // buffer `rbuf` into the other operand buffer (when `do_widen`).
-  auto compute = [&](int obuf, int rbuf, bool zero, auto widen_c) __attribute__((always_inline)) {
+  // buffer `rbuf` into the other operand buffer (when `do_widen`) and issue
+  // the DMA instructions of dma_c.
+  auto compute = [&](int obuf, int rbuf, bool zero, auto widen_c, auto dma_c, int dkt,
+                     int dstage) __attribute__((always_inline)) {
     constexpr bool DO_WIDEN = decltype(widen_c)::value;
+    constexpr int ND = decltype(dma_c)::hi - decltype(dma_c)::lo;
+    constexpr int NMFMA = 2 * FM * FN;
+    constexpr int NVALU = DO_WIDEN ? 12 * (FM + FN) : 0;
+    constexpr int VPM = (NVALU + NMFMA - 1) / NMFMA;
     if (GROUPED && zero) {
-      mma_chunk(obuf, std::true_type{});
-      if constexpr (DO_WIDEN) widen_into(rbuf, 1 - obuf);
+      mma_chunk(obuf, std::true_type{}, dma_c, dkt, dstage);
     } else {
-      mma_chunk(obuf, std::false_type{});
-      if constexpr (DO_WIDEN) widen_into(rbuf, 1 - obuf);
+      mma_chunk(obuf, std::false_type{}, dma_c, dkt, dstage);
+    }
+    if constexpr (DO_WIDEN) widen_into(rbuf, 1 - obuf);
+    // order: each MFMA followed by one DMA instruction (while any remain)
+    // and its share of the widening VALU work
+#pragma unroll
+    for (int k = 0; k < NMFMA; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (k < ND) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      if (VPM > 0) __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
     }
   };
   // Wait until this wave's DMA pieces of a tile have landed; `issued_after`
@@ -336,21 +365,29 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
   // (waited for just before) becomes readable.  Mode kNext: a tile followed
   // by another; kLastFull: the last tile, 256 codes; kLastShort: the last
   // tile, 128 codes.
-  constexpr int kNext = 0, kLastFull = 1, kLastShort = 2;
+  // The DMA of K-tile kt+2 goes into this tile's buffer, free after the
+  // chunk-2 barrier: half of it interleaved with the MFMAs of chunk 2, half
+  // with those of chunk 3; it is waited for at chunk 2 of tile kt+1.
+  constexpr int kNext = 0, kNextNoDma = 1, kLastFull = 2, kLastShort = 3;
+  constexpr int Q1 = LOADS / 2;
+  static_assert(STAGES == 2, "the refill schedule assumes two stages");
+  static_assert(Q1 <= 2 * FM * FN && LOADS - Q1 <= 2 * FM * FN, "one DMA instruction per MFMA at most");
   auto tile = [&](int kt, auto mode_c) __attribute__((always_inline)) {
     constexpr int mode = decltype(mode_c)::value;
+    constexpr bool NEXT = mode == kNext || mode == kNextNoDma;
     const uint8_t *st = smem + (kt % STAGES) * STAGE_BYTES;
     const uint8_t *nst = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
     // groups are whole halves: one can start with half 0 or half 1 and end with either
     const bool start0 = GROUPED && ((2 * kt) % halves_per_group == 0);
     const bool start1 = GROUPED && ((2 * kt + 1) % halves_per_group == 0);
     const bool end1 = GROUPED && ((2 * kt + 2) % halves_per_group == 0);
+    const int dkt = kt + STAGES, dstage = kt % STAGES;   // the tile refilled into this tile's buffer
 
     if constexpr (mode == kLastShort) {
       chunk_fence();
-      compute(0, 1, start0, std::true_type{});
+      compute(0, 1, start0, std::true_type{}, NoDma{}, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      compute(1, 0, false, std::false_type{});
+      compute(1, 0, false, std::false_type{}, NoDma{}, 0, 0);
       if constexpr (GROUPED) {   // the last half ends the last group
         if constexpr (SCALES) read_scales(st, 0);
         group_end(kt, 0);
@@ -361,12 +398,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
       chunk_fence();
       read_raw(st, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
-      compute(0, 1, start0, std::true_type{});
+      compute(0, 1, start0, std::true_type{}, NoDma{}, 0, 0);
       // chunk 1
       chunk_fence();
       read_raw(st, 3, 1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(1, 0, false, std::true_type{});
+      compute(1, 0, false, std::true_type{}, NoDma{}, 0, 0);
       if constexpr (GROUPED) {
         if (start1) {   // half 0 closes a group
           if constexpr (SCALES) read_scales(st, 0);
@@ -379,24 +416,29 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
         // this stage is refilled after the barrier below: take the scales first
         if (end1) read_scales(st, 1);
       }
-      if constexpr (mode == kNext) {
-        wait_tile(min(STAGES - 2, KT - 2 - kt));
+      if constexpr (NEXT) {
+        wait_vm<0>();   // tile kt+1 has landed
         wait_lgkm0();
         __builtin_amdgcn_s_barrier();
-        if (kt + STAGES < KT) issue(kt + STAGES, kt % STAGES);
         read_raw(nst, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      compute(0, 1, start1, std::true_type{});
+      if constexpr (mode == kNext)
+        compute(0, 1, start1, std::true_type{}, DmaRange<0, Q1>{}, dkt, dstage);
+      else
+        compute(0, 1, start1, std::true_type{}, NoDma{}, 0, 0);
       // chunk 3
-      if constexpr (mode == kNext) {
+      if constexpr (NEXT) {
         chunk_fence();
         read_raw(nst, 1, 1);
         __builtin_amdgcn_sched_barrier(0);
-        compute(1, 0, false, std::true_type{});
+        if constexpr (mode == kNext)
+          compute(1, 0, false, std::true_type{}, DmaRange<Q1, LOADS>{}, dkt, dstage);
+        else
+          compute(1, 0, false, std::true_type{}, NoDma{}, 0, 0);
       } else {
         __builtin_amdgcn_sched_barrier(0);
-        compute(1, 0, false, std::false_type{});
+        compute(1, 0, false, std::false_type{}, NoDma{}, 0, 0);
       }
       if constexpr (GROUPED) {
         if (end1) group_end(kt, 1);
@@ -415,7 +457,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
   read_raw(smem, 1, 1);
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int kt = 0; kt + 1 < KT; ++kt) tile(kt, std::integral_constant<int, kNext>{});
+  // Tiles followed by another (refilling their buffer while one remains),
+  // then the last tile, peeled.
+  int kt = 0;
+  for (; kt + STAGES < KT; ++kt) tile(kt, std::integral_constant<int, kNext>{});
+  for (; kt + 1 < KT; ++kt) tile(kt, std::integral_constant<int, kNextNoDma>{});
   if constexpr (SHORT_TAIL)
     tile(KT - 1, std::integral_constant<int, kLastShort>{});
   else
@@ -548,7 +594,12 @@ hipError_t launch_gemm_prefill(const uint8_t *a, const float *sa, const uint8_t 
     const int64_t rounds = (tiles + slots - 1) / slots;
     return (double)tiles / (double)(rounds * slots) * (double)(M * N) / (double)(tm * bm * tn * bn) * size_pref;
   };
-  const double s_128x192 = score(128, 192, 2, 1.0), s_128x128 = score(128, 128, 2, 0.9);
+  // 256 x 192 blocks of 8 waves run one to a CU and move the fewest bytes
+  // per multiply-add; the 4-wave shapes (two to a CU) fill small grids better.
+  const double s_256x192 = score(256, 192, 1, 1.0), s_128x192 = score(128, 192, 2, 0.95),
+               s_128x128 = score(128, 128, 2, 0.93);
+  if (s_256x192 >= s_128x192 && s_256x192 >= s_128x128)
+    return launch_cfg<256, 192, 4, 2, 2, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
   if (s_128x192 >= s_128x128)
     return launch_cfg<128, 192, 2, 2, 2, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
   return launch_cfg<128, 128, 2, 2, 2, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);

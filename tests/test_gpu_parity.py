@@ -280,6 +280,42 @@ def test_gemm_unaligned_output(qr, M, N, K, group):
     check_output(yb[:, 1:N + 1], O.dequantize_output(O.int_gemm(qa, qw, group), sa, sw, group))
 
 
+def _sample_idx(n, tile, rng, k):
+    """Sorted distinct indices: the first and last, both sides of a few tile
+    boundaries, and random ones."""
+    idx = {0, n - 1}
+    for b in range(tile, n, max(tile, (n // 4) // tile * tile)):
+        idx.update((b - 1, b))
+    idx.update(rng.integers(0, n, size=k).tolist())
+    return np.array(sorted(i for i in idx if 0 <= i < n))
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c4"])
+def test_gemm_full_size_sampled(qr, cfg):
+    """The GEMM at the layer's full size, launched exactly as the benchmark
+    launches it, checked against the oracle on a sampled block of outputs
+    (rows across M-tiles and the last row, columns across N-tiles and the
+    last column); the other outputs must be finite."""
+    c = W.CONFIGS[cfg]
+    M, N, K, group = c.M, c.N, c.K, c.group
+    G = 1 if group == 0 else K // group
+    a = W.make_random_packed(M, K // 2, seed=11)
+    w = W.make_random_packed(N, K // 2, seed=12)
+    sa = W.make_random_scales(M * G, 13).reshape(M, G)
+    sw = W.make_random_scales(N * G, 14).reshape(N, G)
+    if group == 0:
+        sa, sw = sa[:, 0].copy(), sw[:, 0].copy()
+    y = qr.int4_gemm(dev(a), dev(sa), dev(w), dev(sw), group)
+    rng = np.random.default_rng(c.index)
+    rows = _sample_idx(M, 128, rng, 40)
+    cols = _sample_idx(N, 192, rng, 60)
+    got = host(y[torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(cols, device="cuda")])
+    acc = O.int_gemm(O.unpack_int4(a[rows]), O.unpack_int4(w[cols]), group)
+    ref = O.dequantize_output(acc, sa[rows], sw[cols], group)
+    check_output(got, ref)
+    assert bool(torch.isfinite(y).all())
+
+
 # ------------------------------------------------------------------ whole layer, GPU path end to end
 
 def layer_gpu(qr, x, w, rot, group):

@@ -224,3 +224,24 @@ def make_random_rows(rows: int, n: int, seed: int, scale: float = 1.0) -> np.nda
 def make_random_codes(rows: int, k: int, seed: int, lo: int = -8, hi: int = 7) -> np.ndarray:
     """Uniform integer codes in [lo, hi] (int8 [rows, k]) for integer-GEMM tests."""
     return _rng(901, seed).integers(lo, hi + 1, size=(rows, k)).astype(np.int8)
+
+
+def make_random_packed(rows: int, nbytes: int, seed: int) -> np.ndarray:
+    """Uniform random bytes (uint8 [rows, nbytes]): two independent uniform
+    4-bit codes per byte, for full-size integer-GEMM inputs."""
+    out = np.empty((rows, nbytes), np.uint8)
+    step = 8192
+
+    def fill(b):
+        r = _rng(902, seed, b)
+        out[b * step:(b + 1) * step] = r.integers(0, 256, size=(min(step, rows - b * step), nbytes), dtype=np.uint8)
+
+    with _cf.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range((rows + step - 1) // step)))
+    return out
+
+
+def make_random_scales(n: int, seed: int, lo: float = 0.001, hi: float = 0.05) -> np.ndarray:
+    """Uniform positive float32 scales in [lo, hi)."""
+    return (_rng(903, seed).random(n) * (hi - lo) + lo).astype(np.float32)
+
