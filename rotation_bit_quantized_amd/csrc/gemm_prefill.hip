@@ -118,7 +118,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
   // one scale set (s_x of the BM rows, then s_w of the BN columns) per K-tile half
   constexpr int SCALE_BYTES = SCALES ? 2 * ROWS * 4 : 0;
   constexpr int SCALE_INST = SCALES ? 2 * ROWS / 64 : 0;   // 4-byte DMA wave-instructions per stage
-  constexpr int STAGE_BYTES = ROWS * kRowBytes + SCALE_BYTES;
+  constexpr int STAGE_BYTES = ROWS * kRowBytes;
+  // the scales live in a ring of three slots after the stages (K-tile kt in
+  // slot kt % 3): the refill of tile kt+2 then never touches the scales of
+  // tiles kt and kt+1, which group epilogues may still read
+  constexpr int SCALE_SLOTS = SCALES ? 3 : 0;
   static_assert(!SCALES || (ROWS % 32 == 0 && SCALE_INST % NW == 0), "scale DMA split");
   constexpr int SCALE_LOADS = SCALE_INST / NW;
   constexpr int TI = ROWS / 8;                    // DMA wave-instructions per stage (8 rows each)
@@ -130,7 +134,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
   static_assert(WAVE_LOADS * (STAGES - 1) < 64, "vmcnt range");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES + SCALE_SLOTS * SCALE_BYTES];
+  uint8_t *const scale_ring = smem + STAGES * STAGE_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
           const float *p = ee < BM ? sa + (int64_t)min(m0 + ee, M - 1) * G + gidx
                                    : sw + (int64_t)min(n0 + ee - BM, N - 1) * G + gidx;
           __builtin_amdgcn_global_load_lds((const void *)p,
-                                           (lds_void *)(smem + stage * STAGE_BYTES + ROWS * kRowBytes +
+                                           (lds_void *)(scale_ring + (kt % 3) * SCALE_BYTES +
                                                         256 * (NW * qs + wave)),
                                            4, 0, 0);
         }
@@ -308,8 +313,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
   // (s_w pre-multiplied by the 1/256 of the widening).
   v4f gsa[SCALES ? FM : 1][4];
   float gsw[SCALES ? FN : 1];
-  auto read_scales = [&](const uint8_t *st, int h) __attribute__((always_inline)) {
-    const float *sc = (const float *)(st + ROWS * kRowBytes) + h * ROWS;
+  auto read_scales = [&](int kt, int h) __attribute__((always_inline)) {
+    const float *sc = (const float *)(scale_ring + (kt % 3) * SCALE_BYTES) + h * ROWS;
 #pragma unroll
     for (int j = 0; j < FN; ++j) gsw[j] = sc[BM + wn * WN + j * 32 + lcol] * (1.0f / 256.0f);
 #pragma unroll
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
       __builtin_amdgcn_sched_barrier(0);
       compute(1, 0, false, std::false_type{}, NoDma{}, 0, 0);
       if constexpr (GROUPED) {   // the last half ends the last group
-        if constexpr (SCALES) read_scales(st, 0);
+        if constexpr (SCALES) read_scales(kt, 0);
         group_end(kt, 0);
       }
       return;
@@ -406,16 +411,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
       compute(1, 0, false, std::true_type{}, NoDma{}, 0, 0);
       if constexpr (GROUPED) {
         if (start1) {   // half 0 closes a group
-          if constexpr (SCALES) read_scales(st, 0);
+          if constexpr (SCALES) read_scales(kt, 0);
           group_end(kt, 0);
         }
       }
       // chunk 2
       chunk_fence();
-      if constexpr (SCALES) {
-        // this stage is refilled after the barrier below: take the scales first
-        if (end1) read_scales(st, 1);
-      }
       if constexpr (NEXT) {
         wait_vm<0>();   // tile kt+1 has landed
         wait_lgkm0();
@@ -441,7 +442,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
         compute(1, 0, false, std::false_type{}, NoDma{}, 0, 0);
       }
       if constexpr (GROUPED) {
-        if (end1) group_end(kt, 1);
+        if (end1) {
+          if constexpr (SCALES) read_scales(kt, 1);
+          group_end(kt, 1);
+        }
       }
     }
   };
