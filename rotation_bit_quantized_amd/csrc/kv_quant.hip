@@ -12,11 +12,12 @@
 //   q = clamp(rint(u * 15/(hi - lo)) + z, 0, 15)
 //
 // The whole 128-point transform is one pass of v_mfma_f32_16x16x32_f16
-// (input fp16 is exact, H entries +-1 are exact, sums in fp32): A = 16
-// vectors x 128 (one 16-byte load per lane per k-step), B = H_128 held in
-// registers with its columns permuted so that lane (c16, g) receives outputs
-// j = 8*c16 + nt for the 8 N-tiles nt - eight consecutive outputs per lane,
-// packed into one 32-bit word of codes per vector.
+// (input fp16 is exact, H entries +-1 are exact, sums in fp32), computed
+// transposed: A = H_128 with its rows (the output index) permuted, held in
+// registers; B = 16 vectors of the tile as columns (one 16-byte load per lane
+// per k-step); C[output][vector].  With the permutation, lane (c16, g) holds
+// outputs 32 g .. 32 g + 31 of vector c16: the range reduction needs two
+// cross-lane steps, and the 32 codes leave as one 16-byte store.
 #include "qr_common.h"
 #include "qr_launch.h"
 
@@ -32,17 +33,20 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
   const int c16 = lane & 15;
   const int g = lane >> 4;
 
-  // B[s][nt]: slot j holds H[k][jj], k = 32 s + 8 g + j, jj = 8 c16 + nt.
-  v8h bop[4][8];
+  // A[mt][s]: this lane's row c16 of M-tile mt is output
+  // jj = 32 (c16 >> 2) + 4 mt + (c16 & 3); slot j holds H[k][jj] for
+  // k = 32 s + 8 g + j.  (C row 4 g' + r of M-tile mt is then output
+  // 32 g' + 4 mt + r.)
+  v8h hop[8][4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int k = 32 * s + 8 * g + j;
-        const int jj = 8 * c16 + nt;
-        bop[s][nt][j] = (__builtin_popcount(k & jj) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+        const int jj = 32 * (c16 >> 2) + 4 * mt + (c16 & 3);
+        hop[mt][s][j] = (__builtin_popcount(k & jj) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
       }
   // sign masks for this lane's k-range 32 s + 8 g + 0..7 (two aligned words)
   unsigned smask[4][4];
@@ -69,21 +73,29 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
   const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerBlock;
   const unsigned magic = f2u(kRoundMagic);
 
-  for (int64_t tile = wave_id; tile < ntiles; tile += wave_stride) {
-    // A: this lane loads row c16 of the tile (vector v), k-range 8 g + 32 s.
+  // B: this lane loads vector c16 of a tile, elements 32 s + 8 g .. + 7.
+  // The next tile's loads are issued before this tile is computed, so a
+  // wave always has a tile in flight.
+  auto load_tile = [&](int64_t tile, v4u (&raw)[4]) {
     const int64_t v = tile * 16 + c16;
     const bool valid = v < nvec;
     const int64_t vt = valid ? v / H : 0;
     const int vh = valid ? (int)(v - vt * H) : 0;
     const unsigned short *src = kv + vt * ld_kv + vh * 128 + 8 * g;
-    v4u raw[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       raw[s] = valid ? __builtin_nontemporal_load((const v4u *)(src + 32 * s)) : v4u{0u, 0u, 0u, 0u};
+  };
+  v4u raw[4];
+  if (wave_id < ntiles) load_tile(wave_id, raw);
+
+  for (int64_t tile = wave_id; tile < ntiles; tile += wave_stride) {
+    v4u nxt[4];
+    if (tile + wave_stride < ntiles) load_tile(tile + wave_stride, nxt);
 
     v4f c[8];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) c[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 8; ++mt) c[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       v4u w = raw[s];
@@ -91,45 +103,51 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
       w[1] ^= smask[s][1];
       w[2] ^= smask[s][2];
       w[3] ^= smask[s][3];
-      const v8h a = __builtin_bit_cast(v8h, w);
+      const v8h b = __builtin_bit_cast(v8h, w);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[s][nt], c[nt], 0, 0, 0);
+      for (int mt = 0; mt < 8; ++mt) c[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hop[mt][s], b, c[mt], 0, 0, 0);
     }
 
-    // Output vector row 4 g + r of the tile, outputs 8 c16 + nt.
+    // c[mt][r] = output 32 g + 4 mt + r of vector c16.  Range widened to
+    // include 0, over the lane's 32 outputs, then over the 4 lanes g.
+    float mn = 0.f, mx = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float mn = 0.f, mx = 0.f;  // range widened to include 0
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        mn = fminf(mn, c[nt][r]);
-        mx = fmaxf(mx, c[nt][r]);
+      for (int r = 0; r < 4; ++r) {
+        mn = fminf(mn, c[mt][r]);
+        mx = fmaxf(mx, c[mt][r]);
       }
+    mn = fminf(mn, __shfl_xor(mn, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mn = fminf(mn, __shfl_xor(mn, 32, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float rng = mx - mn;
+    const float inv = rng > 0.f ? 15.0f / rng : 0.f;
+    const int z = rng > 0.f ? (int)rintf(-mn * inv) : 0;
+    const unsigned bias = magic - (unsigned)z;  // bits(fma) - bias = rint(u*inv) + z
+    unsigned word[4];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, o, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      }
-      const float rng = mx - mn;
-      const float inv = rng > 0.f ? 15.0f / rng : 0.f;
-      const int z = rng > 0.f ? (int)rintf(-mn * inv) : 0;
-      const unsigned bias = magic - (unsigned)z;  // bits(fma) - bias = rint(u*inv) + z
-      unsigned word = 0;
+    for (int wd = 0; wd < 4; ++wd) {
+      unsigned acc = 0;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        int q = (int)(round_bits(c[nt][r], inv) - bias);
+      for (int t = 0; t < 8; ++t) {   // output 32 g + 8 wd + t = mt 2 wd + t/4, r t%4
+        int q = (int)(round_bits(c[2 * wd + (t >> 2)][t & 3], inv) - bias);
         q = min(15, max(0, q));
-        word |= (unsigned)q << (4 * nt);
+        acc |= (unsigned)q << (4 * t);
       }
-      const int64_t vo = tile * 16 + 4 * g + r;
-      if (vo < nvec) {
-        *(unsigned *)(codes + vo * 64 + 4 * c16) = word;
-        if (c16 == 0) {
-          scales[vo] = rng * step_mul;
-          zeros[vo] = (uint8_t)z;
-        }
+      word[wd] = acc;
+    }
+    const int64_t vo = tile * 16 + c16;
+    if (vo < nvec) {
+      *(v4u *)(codes + vo * 64 + 16 * g) = v4u{word[0], word[1], word[2], word[3]};
+      if (g == 0) {
+        scales[vo] = rng * step_mul;
+        zeros[vo] = (uint8_t)z;
       }
     }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) raw[s] = nxt[s];
   }
 }
 
@@ -141,9 +159,19 @@ hipError_t launch_kv_quant(const void *kv, int64_t T, int64_t H, int64_t ld_kv, 
   (void)hipGetDevice(&dev);
   int cus = 256;
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  // persistent grid: as many blocks as are resident at once, each wave
+  // walking its tiles with the next one always in flight
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kv_quant_kernel, 64 * kWavesPerBlock, 0) != hipSuccess ||
+        b < 1)
+      b = 1;
+    per_cu = b;
+  }
   const int64_t tiles = (T * H + 15) / 16;
   const int64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t cap = (int64_t)cus * 8;
+  const int64_t cap = (int64_t)cus * per_cu;
   const int64_t grid = blocks < cap ? blocks : cap;
   const float step_mul = (float)(1.0 / (15.0 * __builtin_sqrt(128.0)));
   kv_quant_kernel<<<dim3((unsigned)grid), dim3(64 * kWavesPerBlock), 0, stream>>>(

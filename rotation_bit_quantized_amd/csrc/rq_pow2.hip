@@ -7,15 +7,19 @@
 // byte (QuaRot summary, "Key points": RTN on the fly; group size 128).
 //
 // Design (one wave per token row, rows grid-strided over a persistent grid):
+//  * Data path: each wave owns two one-row LDS buffers.  Rows are brought in
+//    by global_load_lds_dwordx4 (no VGPR staging); as soon as pass 1 has
+//    read a buffer, the DMA of the wave's row after next is issued into it,
+//    so two rows stream from HBM while the wave works on a third.
 //  * Element index bits e0..e(L-1).  Since H_n[e][f] = (-1)^popcount(e & f),
 //    the transform factors over any split of the bits into two sets; here
 //      i_b = {e0, e1, e6, e7, e8, e9}   (64-point factor, on MFMA)
 //      i_a = {e2..e5, e10..e(L-1)}       (the rest, in registers)
 //  * Pass 1: v_mfma_f32_16x16x32_f16 with A = the fp16 input (exact, sign-
-//    flipped by XOR) and B = the +-1 64-point factor.  Each lane loads 8-byte
+//    flipped by XOR) and B = the +-1 64-point factor.  Each lane reads 8-byte
 //    pieces: lane bits 0..3 select e2..e5 (rows of A), lane bits 4..5 select
 //    e6, e7 (k-groups), the two 8-byte halves select e8, the k-step e9 and the
-//    M-tile e10.. - so every load instruction reads 512 contiguous bytes.
+//    M-tile e10.. - so every LDS read instruction covers 512 contiguous bytes.
 //  * B's columns are permuted so that the MFMA output puts e0, e1 in the
 //    N-tile index and e6..e9 in lane bits 0..3; the output rows carry e2, e3
 //    in the register index and e4, e5 in lane bits 4, 5.
@@ -32,7 +36,7 @@
 namespace qr {
 namespace {
 
-constexpr int kWavesPerBlock = 4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void swap16(float &a, float &b) {
   auto r = __builtin_amdgcn_permlane16_swap(f2u(a), f2u(b), false, false);
@@ -45,18 +49,47 @@ __device__ __forceinline__ void swap32(float &a, float &b) {
   b = u2f(r[1]);
 }
 
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Four waves per block, each with two row buffers: two of its rows stream in
+// while it works on a third.  n = 4096: 64 KB per block, two blocks per CU;
+// n = 8192: 128 KB, one block per CU.
+constexpr int kWaves = 4;
+constexpr int kBufs = 2;
+
+template <int L>
+constexpr int lds_bytes() {
+  return kWaves * kBufs * (2 << L);
+}
+
 // Register index of a value: bits 0-1 = r (MFMA output row within the 4-row
 // group), bits 2-3 = N-tile, bits 4.. = M-tile.
 template <int L, int GROUP>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void rq_pow2_kernel(
+__global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
     const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, const int8_t *__restrict__ signs,
     uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
   constexpr int n = 1 << L;
-  constexpr int MT = 1 << (L - 10);  // M-tiles of 16 rows of the 64-column view
-  constexpr int NV = MT * 16;        // values per lane
+  constexpr int ROWB = 2 * n;         // bytes per input row
+  constexpr int DMA = ROWB / 1024;    // 1 KB DMA wave-instructions per row
+  constexpr int MT = 1 << (L - 10);   // M-tiles of 16 rows of the 64-column view
+  constexpr int NV = MT * 16;         // values per lane
+  constexpr int RUNS = NV / 64;
+  // vector-memory instructions per row after its compute: two 16-byte code
+  // stores per run, then the scale stores (one per run for groups)
+  constexpr int STORES = 2 * RUNS + (GROUP == 0 ? 1 : RUNS);
   static_assert(L == 12 || L == 13, "pass-2 layout written for n = 4096, 8192");
+  static_assert(2 * STORES + DMA < 64, "vmcnt range");
 
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<L>()];
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t *const bufs = smem + wave * kBufs * ROWB;
+
   const int c16 = lane & 15;
   const int g = lane >> 4;
 
@@ -74,53 +107,65 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void rq_pow2_kernel(
         bop[s][nt][j] = (par & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
       }
 
-  // Sign masks for the pieces this lane loads: piece (m, s, h) covers
+  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t wave_stride = (int64_t)gridDim.x * kWaves;
+  if (wave_id >= rows) return;
+
+  // DMA of row r into buffer b.  Rows past the end are clamped to the last
+  // row (their buffers are never read), which keeps the number of vector
+  // memory instructions per row uniform and the vmcnt waits below exact.
+  auto issue_row = [&](int64_t r, int b) {
+    const uint8_t *src = (const uint8_t *)(x + (r < rows ? r : rows - 1) * ld_x);
+#pragma unroll
+    for (int i = 0; i < DMA; ++i)
+      __builtin_amdgcn_global_load_lds((const void *)(src + 1024 * i + 16 * lane),
+                                       (lds_void *)(bufs + b * ROWB + 1024 * i), 16, 0, 0);
+  };
+
+  issue_row(wave_id, 0);
+  issue_row(wave_id + wave_stride, 1);
+
+  // Sign masks for the pieces this lane reads: piece (m, s, h) covers
   // elements base + 0..3 with base = 4 c16 + 64 g + 256 h + 512 s + 1024 m;
   // their four int8 signs are one aligned 32-bit word.
   unsigned smask[MT][2][2][2];
-  if (signs != nullptr) {
-    unsigned sw[MT][2][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        smask[m][s][h][0] = smask[m][s][h][1] = 0u;
+        if (signs != nullptr)
+          sign_masks4(*(const unsigned *)(signs + 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m),
+                      smask[m][s][h][0], smask[m][s][h][1]);
+      }
+
+  wait_vm<0>();   // the sign words (and the first two rows) are in: no wait on them inside the loop
+
+  int it = 0;
+  for (int64_t row = wave_id; row < rows; row += wave_stride, ++it) {
+    const uint8_t *buf = bufs + (it & 1) * ROWB;
+    // Wait for this row's DMA.  Issued after it: the DMA of the following
+    // row (always), the stores of the previous row (it >= 1) and of the one
+    // before, with the DMA of this row's follower in between (it >= 2).
+    if (it == 0) wait_vm<DMA>();
+    else if (it == 1) wait_vm<DMA + STORES>();
+    else wait_vm<DMA + 2 * STORES>();
+
+    // ---- pass 1: 64-point factor on MFMA, A read from the LDS row buffer
+    v2u pc[MT][2][2];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          sw[m][s][h] = *(const unsigned *)(signs + 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m);
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) sign_masks4(sw[m][s][h], smask[m][s][h][0], smask[m][s][h][1]);
-  } else {
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) smask[m][s][h][0] = smask[m][s][h][1] = 0u;
-  }
+          pc[m][s][h] = *(const v2u *)(buf + 2 * (4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m));
+    // every read has returned: the buffer takes the row after next
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    issue_row(row + 2 * wave_stride, it & 1);
 
-  const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerBlock;
-
-  for (int64_t row = wave_id; row < rows; row += wave_stride) {
-    const unsigned short *xr = x + row * ld_x;
-
-    // ---- loads (all issued before the first MFMA)
-    v2u piece[MT][2][2];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int base = 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m;
-          piece[m][s][h] = __builtin_nontemporal_load((const v2u *)(xr + base));
-        }
-
-    // ---- pass 1: 64-point factor on MFMA
     float v[NV];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -128,10 +173,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void rq_pow2_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         v4u w;
-        w[0] = piece[m][s][0][0] ^ smask[m][s][0][0];
-        w[1] = piece[m][s][0][1] ^ smask[m][s][0][1];
-        w[2] = piece[m][s][1][0] ^ smask[m][s][1][0];
-        w[3] = piece[m][s][1][1] ^ smask[m][s][1][1];
+        w[0] = pc[m][s][0][0] ^ smask[m][s][0][0];
+        w[1] = pc[m][s][0][1] ^ smask[m][s][0][1];
+        w[2] = pc[m][s][1][0] ^ smask[m][s][1][0];
+        w[3] = pc[m][s][1][1] ^ smask[m][s][1][1];
         a[s] = __builtin_bit_cast(v8h, w);
       }
 #pragma unroll
@@ -178,7 +223,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void rq_pow2_kernel(
 
     // Lane now owns outputs e = 64*lane + f(i) (+ 4096 * bit6 of i for L=13)
     // with f(i) = ((i>>2)&3) | (i&3)<<2 | ((i>>4)&3)<<4.
-    constexpr int RUNS = NV / 64;
     float amax[RUNS];
 #pragma unroll
     for (int run = 0; run < RUNS; ++run) {
@@ -194,14 +238,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void rq_pow2_kernel(
       mx = wave_max(mx);
 #pragma unroll
       for (int run = 0; run < RUNS; ++run) amax[run] = mx;
-      if (lane == 0) scales[row] = mx * scale_mul;
     } else {
       // a group of 128 spans lanes 2q, 2q+1 of one run
 #pragma unroll
-      for (int run = 0; run < RUNS; ++run) {
-        amax[run] = fmaxf(amax[run], __shfl_xor(amax[run], 1, 64));
-        if ((lane & 1) == 0) scales[row * (n / 128) + run * 32 + (lane >> 1)] = amax[run] * scale_mul;
-      }
+      for (int run = 0; run < RUNS; ++run) amax[run] = fmaxf(amax[run], __shfl_xor(amax[run], 1, 64));
     }
 
     uint8_t *cr = codes + row * (int64_t)(n / 2);
@@ -224,7 +264,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void rq_pow2_kernel(
       dst[0] = v4u{words[0], words[1], words[2], words[3]};
       dst[1] = v4u{words[4], words[5], words[6], words[7]};
     }
+    if (GROUP == 0) {
+      if (lane == 0) scales[row] = amax[0] * scale_mul;
+    } else {
+#pragma unroll
+      for (int run = 0; run < RUNS; ++run)
+        if ((lane & 1) == 0) scales[row * (n / 128) + run * 32 + (lane >> 1)] = amax[run] * scale_mul;
+    }
   }
+  wait_vm<0>();   // no DMA may still be writing this block's LDS when it exits
 }
 
 template <int L, int GROUP>
@@ -234,11 +282,20 @@ hipError_t launch_one(const void *x, int64_t rows, int64_t ld_x, const int8_t *s
   (void)hipGetDevice(&dev);
   int cus = 256;
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int64_t blocks_needed = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t cap = (int64_t)cus * 8;
+  // persistent grid: as many blocks as are resident at once
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rq_pow2_kernel<L, GROUP>, 64 * kWaves, 0) != hipSuccess ||
+        b < 1)
+      b = 1;
+    per_cu = b;
+  }
+  const int64_t blocks_needed = (rows + kWaves - 1) / kWaves;
+  const int64_t cap = (int64_t)cus * per_cu;
   const int64_t grid = blocks_needed < cap ? blocks_needed : cap;
   const float scale_mul = (float)(1.0 / (7.0 * __builtin_sqrt((double)(1 << L))));
-  rq_pow2_kernel<L, GROUP><<<dim3((unsigned)grid), dim3(64 * kWavesPerBlock), 0, stream>>>(
+  rq_pow2_kernel<L, GROUP><<<dim3((unsigned)grid), dim3(64 * kWaves), 0, stream>>>(
       (const unsigned short *)x, rows, ld_x, signs, codes, scales, scale_mul);
   return hipGetLastError();
 }
