@@ -104,10 +104,11 @@ __device__ __forceinline__ void tile_of(int bid, int tm_count, int tn_count, int
   tn = in_band / gm;
 }
 
-// Blocks of 4 waves run two to a CU, blocks of 8 waves one: two waves per
-// SIMD either way.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GROUPED, bool OUT_I32, bool SHORT_TAIL>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) void gemm_prefill_kernel(
+// OCC waves per SIMD: blocks of 4 waves run OCC to a CU, blocks of 8 waves
+// OCC/2.  At OCC 1 a wave has the whole register file (AGPR accumulators).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GROUPED, bool OUT_I32, bool SHORT_TAIL,
+          int OCC = 2>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_N)) void gemm_prefill_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ W,
     const float *__restrict__ sw, int M, int N, int K, int group, void *__restrict__ out, int64_t ld_y) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -272,8 +273,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(opA[obuf][i][ks], opB[obuf][j][ks], v16i{}, 0, 0, 0);
           else
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(opA[obuf][i][ks], opB[obuf][j][ks], acc[i][j], 0, 0, 0);
+          // DMA instructions spaced evenly over the chunk's MFMAs: after
+          // MFMA idx when idx is a multiple of the spacing
+          constexpr int NMF = 2 * FM * FN, ND = Q_HI - Q_LO;
+          constexpr int SP = ND > 0 ? (NMF / ND > 0 ? NMF / ND : 1) : 1;
           const int idx = (ks * FM + i) * FN + j;
-          if (Q_LO + idx < Q_HI) issue_q(dkt, dstage, Q_LO + idx);
+          if (idx % SP == 0 && idx / SP < ND) issue_q(dkt, dstage, Q_LO + idx / SP);
         }
   };
   // Multiply operand buffer `obuf` and, interleaved with it, widen raw
@@ -292,12 +297,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
       mma_chunk(obuf, std::false_type{}, dma_c, dkt, dstage);
     }
     if constexpr (DO_WIDEN) widen_into(rbuf, 1 - obuf);
-    // order: each MFMA followed by one DMA instruction (while any remain)
-    // and its share of the widening VALU work
+    // order: MFMAs with the DMA instructions spread evenly between them and
+    // the widening VALU work shared out
+    constexpr int SP = ND > 0 ? (NMFMA / ND > 0 ? NMFMA / ND : 1) : 1;
 #pragma unroll
     for (int k = 0; k < NMFMA; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (k < ND) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      if (k % SP == 0 && k / SP < ND) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
       if (VPM > 0) __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
     }
   };
@@ -558,7 +564,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 8 / (WAVES_M * WAVES_N)) vo
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GROUPED>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GROUPED, int OCC = 2>
 hipError_t launch_cfg(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw, int64_t M,
                       int64_t N, int64_t K, int group, void *y, int64_t ld_y, bool out_i32,
                       hipStream_t stream) {
@@ -566,7 +572,7 @@ hipError_t launch_cfg(const uint8_t *a, const float *sa, const uint8_t *w, const
   dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
   const bool short_tail = K % kBK != 0;
 #define QR_GEMM_LAUNCH(I32, TAIL)                                                                \
-  gemm_prefill_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, GROUPED, I32, TAIL><<<grid, block, 0, stream>>>( \
+  gemm_prefill_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, GROUPED, I32, TAIL, OCC><<<grid, block, 0, stream>>>( \
       a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y)
   if (out_i32) {
     if (short_tail) QR_GEMM_LAUNCH(true, true);
