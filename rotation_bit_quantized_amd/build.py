@@ -29,13 +29,21 @@ CFLAGS = [
 ]
 
 
+# Per-file additions.  The Kronecker kernel keeps its MFMA accumulators in
+# VGPRs (the VALU transform works on them in place) and its B operands in
+# AGPRs.
+EXTRA_FLAGS = {
+    "rq_kron.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> tuple[str, str]:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{p.stdout}\n{p.stderr}")

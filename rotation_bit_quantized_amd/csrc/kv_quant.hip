@@ -26,6 +26,40 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
+// The A operands (permuted H_128) of every lane, computed at compile time:
+// entry [mt][s][lane] is the v8h of M-tile mt, k-step s for lane (c16, g):
+// slot j holds H[32 s + 8 g + j][32 (c16 >> 2) + 4 mt + (c16 & 3)] as fp16
+// +-1 (0x3C00 / 0xBC00), two per 32-bit word.  Loading it (32 KB, coalesced,
+// cache resident after the first waves) replaces ~1500 VALU ops per wave of
+// operand construction, which matter when a wave has only a few tiles.
+struct HopTable {
+  unsigned w[8][4][64][4];
+};
+constexpr HopTable make_hop_table() {
+  HopTable t{};
+  for (int mt = 0; mt < 8; ++mt)
+    for (int s = 0; s < 4; ++s)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int c16 = lane & 15, g = lane >> 4;
+        const int jj = 32 * (c16 >> 2) + 4 * mt + (c16 & 3);
+        for (int d = 0; d < 4; ++d) {
+          unsigned word = 0;
+          for (int half = 0; half < 2; ++half) {
+            const int k = 32 * s + 8 * g + 2 * d + half;
+            int bits = k & jj, par = 0;
+            while (bits) {
+              par ^= bits & 1;
+              bits >>= 1;
+            }
+            word |= (par ? 0xBC00u : 0x3C00u) << (16 * half);
+          }
+          t.w[mt][s][lane][d] = word;
+        }
+      }
+  return t;
+}
+__device__ constexpr HopTable kHop = make_hop_table();
+
 __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
     const unsigned short *__restrict__ kv, int64_t T, int H, int64_t ld_kv, const int8_t *__restrict__ signs,
     uint8_t *__restrict__ codes, float *__restrict__ scales, uint8_t *__restrict__ zeros, float step_mul) {
@@ -41,13 +75,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int k = 32 * s + 8 * g + j;
-        const int jj = 32 * (c16 >> 2) + 4 * mt + (c16 & 3);
-        hop[mt][s][j] = (__builtin_popcount(k & jj) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
-      }
+    for (int s = 0; s < 4; ++s) hop[mt][s] = __builtin_bit_cast(v8h, *(const v4u *)kHop.w[mt][s][lane]);
   // sign masks for this lane's k-range 32 s + 8 g + 0..7 (two aligned words)
   unsigned smask[4][4];
   if (signs != nullptr) {

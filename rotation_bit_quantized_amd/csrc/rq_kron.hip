@@ -12,197 +12,469 @@
 // is Y = H_64^T X O / 8: a dense m x m product per token, then a 64-point
 // Walsh-Hadamard transform over the row index.
 //
-// Design (one wave per token row, four waves per block, persistent grid):
-//  * The dense product runs on v_mfma_f32_32x32x16_f16 with A = X (the fp16
-//    input, exact) and B = O split into an fp16 high part and an fp16 low
-//    part (O - hi); both products accumulate into the same fp32
-//    accumulators, which keeps the error near 2^-22 relative (one fp16 pass
-//    alone would round O to 2^-11 and move codes that sit near a rounding
-//    boundary).  K (a) is padded to 16 k-steps of 16, N (b) to 6 N-tiles
-//    of 32 with the column map b = 6 * lane + nt, so each lane ends up with
-//    six consecutive outputs of every row j.
-//  * O's hi/lo B-fragments are laid out once per block in LDS (KS x 6 x 2
-//    KB, 132 KB for m = 172) straight from the fp32 factor.
-//  * The 64-point transform over i: the accumulator rows carry i bits
-//    {0,1,3,4} in the register index and i5 in the M-tile, i2 in lane bit 5;
-//    butterflies in registers, then one v_permlane32_swap brings i2 into a
-//    register bit for the last stage.
-//  * Codes: each lane writes three bytes (six codes) per output row j.
+// Design (one token row at a time per block of four waves, persistent grid,
+// one block per CU):
+//  * The dense product runs on v_mfma_f32_16x16x32_f16 (the last 16 of K on
+//    v_mfma_f32_16x16x16_f16) with A = X (the fp16 input, exact) and B = O
+//    split into an fp16 high part and an fp16 low part (O - hi); both
+//    products accumulate into the same fp32 accumulators (error near 2^-22
+//    relative; one fp16 pass alone would round O to 2^-11 and move codes that
+//    sit near a rounding boundary).  K (a) is padded to 176, N (b) to 192.
+//  * O's B-fragments stay in AGPRs for the whole kernel, split over the
+//    waves: wave w owns N-tiles 3w .. 3w+2 (132 registers of hi/lo parts).
+//  * The X row travels by coalesced global_load_lds DMA (1 KB per wave
+//    instruction, one per k-step) into one of two LDS buffers shared by the
+//    four waves, a row ahead.  M-tile mt holds the rows
+//    i = 32 (mt >> 1) + 2 c + (mt & 1), c < 16: with the 344-byte row pitch
+//    of m = 172, sixteen such rows start in sixteen distinct bank groups.
+//  * Software pipeline over rows with two accumulator sets in VGPRs: while
+//    the MFMAs of row r run, the same wave finishes row r - 1 (64-point
+//    transform, absmax, quantization, code staging) and stores the codes of
+//    row r - 2, interleaved with those MFMAs.
+//  * The 64-point transform over i is in registers: i0, i5 are M-tile bits,
+//    i1, i2 register bits, i3, i4 lane bits 4, 5 brought into register bits
+//    with v_permlane16_swap / v_permlane32_swap.
+//  * The absmax is reduced with DPP and lane swaps, then across the four
+//    waves through LDS.  Codes are packed eight to a word in registers, a
+//    4 x 4 nibble transpose within lane quads (DPP, v_perm, v_alignbit) makes
+//    each 16-bit half four consecutive codes of one output row, and the
+//    block stores the row from LDS as 16-byte chunks.
 #include "qr_common.h"
 #include "qr_launch.h"
+
+#include <type_traits>
 
 namespace qr {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kMaxKS = 11;      // k-steps of 16: m <= 176
-constexpr int kNT = 6;          // N-tiles of 32 columns: b < 192
+typedef __attribute__((address_space(3))) void lds_void;
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+template <int V>
+using IC = std::integral_constant<int, V>;
 
+constexpr int kWaves = 4;
+constexpr int kMT = 4;          // M-tiles of 16 rows i
+constexpr int kKS = 6;          // five k-steps of 32 (a < 160) and one of 16 (a < 176)
+constexpr int kNTW = 3;         // N-tiles of 16 per wave: b < 192
+constexpr int kRowBuf = 23552;  // one X row (<= 22528 bytes) plus the A-read overrun past it
+constexpr int kGroupPitch = 1408;                // LDS bytes per 16 output rows j of codes (16 * 176 / 2)
+constexpr int kCodeOff = 2 * kRowBuf;            // codes of one row, four groups of 16 rows j
+constexpr int kSinkOff = kCodeOff + 4 * kGroupPitch;   // masked-off code writes land here
+constexpr int kMaxOff = kSinkOff + 4 * kGroupPitch;    // the four waves' maxima
+constexpr int kLds = kMaxOff + 16;
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ void swap16(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane16_swap(f2u(a), f2u(b), false, false);
+  a = u2f(r[0]);
+  b = u2f(r[1]);
+}
 __device__ __forceinline__ void swap32(float &a, float &b) {
   auto r = __builtin_amdgcn_permlane32_swap(f2u(a), f2u(b), false, false);
   a = u2f(r[0]);
   b = u2f(r[1]);
 }
 
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return u2f(dpp<CTRL>(f2u(v)));
+}
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Max over the 64 lanes without LDS: DPP within rows of 16, then the
+// row-pair swaps.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));   // lanes i and 7 - i of each half row
+  v = fmaxf(v, dpp<kRowMirror>(v));       // lanes i and 15 - i of each row
+  auto a = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  v = fmaxf(u2f(a[0]), u2f(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  return fmaxf(u2f(b[0]), u2f(b[1]));
+}
+
 __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
     const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, int m, const float *__restrict__ dense,
     uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // [ks][nt][hi/lo][64 lanes][16 B]
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
+  float *const wmax = (float *)(smem + kMaxOff);
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int KS = (m + 15) / 16;
-  const int n = 64 * m;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+  const int rowb = 128 * m;                 // bytes of one X row (64 m fp16)
+  const int nchunks = rowb / 1024 + (rowb % 1024 != 0);   // <= 22 = 4 waves x 6 k-steps - 2
+  const int code_bytes = 32 * m;            // n / 2
+  const int half_m = m >> 1;
 
-  // ---- B-fragments of O (hi and lo fp16 parts), once per block
-  for (int f = tid; f < KS * kNT * 64; f += 64 * kWaves) {
-    const int ks = f / (kNT * 64);
-    const int nt = (f / 64) % kNT;
-    const int l = f % 64;
-    const int b = 6 * (l & 31) + nt;
-    v8h hi, lo;
+  // ---- this wave's B-fragments of O, fp16 hi and lo parts.  32-wide
+  // k-steps: lane (c16, g) holds O[32 ks + 8 g + j][b], j < 8; the 16-wide
+  // last one O[160 + 4 g + j][b], j < 4; b = 16 (3 wave + t) + c16; zero
+  // past m.
+  v8h ob[kNTW][kKS - 1][2];
+  v4h ob5[kNTW][2];
+  auto o_at = [&](int a, int b) __attribute__((always_inline)) {
+    const bool in = a < m && b < m;
+    const float o = dense[in ? a * m + b : 0];   // clamped load, then select
+    return in ? o : 0.f;
+  };
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int a = 16 * ks + 8 * (l >> 5) + s;
-      const float o = (a < m && b < m) ? dense[a * m + b] : 0.f;
+  for (int t = 0; t < kNTW; ++t) {
+    const int b = 16 * (kNTW * wave + t) + c16;
+#pragma unroll
+    for (int ks = 0; ks < kKS - 1; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float o = o_at(32 * ks + 8 * g + j, b);
+        const _Float16 h = (_Float16)o;
+        ob[t][ks][0][j] = h;
+        ob[t][ks][1][j] = (_Float16)(o - (float)h);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float o = o_at(160 + 4 * g + j, b);
       const _Float16 h = (_Float16)o;
-      hi[s] = h;
-      lo[s] = (_Float16)(o - (float)h);
+      ob5[t][0][j] = h;
+      ob5[t][1][j] = (_Float16)(o - (float)h);
     }
-    *(v8h *)(smem + (((ks * kNT + nt) * 2 + 0) * 64 + l) * 16) = hi;
-    *(v8h *)(smem + (((ks * kNT + nt) * 2 + 1) * 64 + l) * 16) = lo;
   }
-  __syncthreads();
 
-  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (tid >> 6);
-  const int64_t wave_stride = (int64_t)gridDim.x * kWaves;
-  const int ri = lane & 31;          // row of A (i within an M-tile), column of C
-  const int h = lane >> 5;           // k-half
+  // O lives in AGPRs (MFMA reads its B operand from there); the VGPRs hold
+  // the two accumulator sets, which the VALU transform works on in place.
+  // (This file is built with MFMA results in VGPRs.)
+#pragma unroll
+  for (int t = 0; t < kNTW; ++t) {
+#pragma unroll
+    for (int ks = 0; ks < kKS - 1; ++ks)
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl) asm volatile("" : "+a"(ob[t][ks][hl]));
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) asm volatile("" : "+a"(ob5[t][hl]));
+  }
+  // A reads that run past a row's DMA'd bytes (small m) must see finite
+  // values (they meet zero columns of O): clear each buffer's tail once.
+  for (int off = rowb + 16 * tid; off + 16 <= kRowBuf; off += 16 * 64 * kWaves) {
+    *(v4u *)(smem + off) = v4u{0u, 0u, 0u, 0u};
+    *(v4u *)(smem + kRowBuf + off) = v4u{0u, 0u, 0u, 0u};
+  }
 
-  for (int64_t row = wave_id; row < rows; row += wave_stride) {
-    const unsigned short *xr = x + row * ld_x;
-    v16f c[2][kNT];
+  // ---- per-lane constants
+  // A: M-tile mt, lane (c16, g) reads row i = 32 (mt >> 1) + 2 c16 + (mt & 1):
+  // with the 344-byte row pitch of m = 172 the sixteen rows of a read start
+  // in sixteen distinct bank groups.
+  int a_off[kMT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < kMT; ++mt) a_off[mt] = (32 * (mt >> 1) + 2 * c16 + (mt & 1)) * 2 * m;
+  // code writes: after the nibble transpose, half h of word (t, R) holds the
+  // codes of row j = g | (c16 & 3) << 2 | h << 4 | R << 5, columns
+  // col .. col + 3 with col = 16 (3 wave + t) + 4 (c16 >> 2); LDS keeps 16
+  // rows j per group of kGroupPitch bytes, group 2 R + h.
+  int cw_off[kNTW];
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) c[mt][nt] = v16f{};
-
-    // ---- dense factor on MFMA: C[i][b] += X[i][a] (O_hi + O_lo)[a][b]
-    v2u nxt[2][2];
-    auto load_a = [&](int ks, v2u (&dst)[2][2]) {
+  for (int t = 0; t < kNTW; ++t) {
+    const int col = 16 * (kNTW * wave + t) + 4 * (c16 >> 2);
+    cw_off[t] = col < m ? kCodeOff + (g | ((c16 & 3) << 2)) * half_m + (col >> 1) : kSinkOff;
+  }
+  // code stores: 16-byte chunks ch = tid, tid + 256 of the row (clamped
+  // duplicates past its end); a chunk never straddles a group (8 m bytes).
+  int cs_lds[2], cs_glb[2];
+  {
+    const int nst = code_bytes / 16;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const unsigned short *p = xr + (32 * mt + ri) * m + 16 * ks + 8 * h;
-        const int a0 = 16 * ks + 8 * h;
-        dst[mt][0] = a0 < m ? *(const v2u *)p : v2u{0u, 0u};
-        dst[mt][1] = a0 + 4 < m ? *(const v2u *)(p + 4) : v2u{0u, 0u};
-      }
-    };
-    load_a(0, nxt);
-    for (int ks = 0; ks < KS; ++ks) {
-      v8h a[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        v4u w = {nxt[mt][0][0], nxt[mt][0][1], nxt[mt][1][0], nxt[mt][1][1]};
-        a[mt] = __builtin_bit_cast(v8h, w);
-      }
-      if (ks + 1 < KS) load_a(ks + 1, nxt);
-      const uint8_t *fb = smem + (ks * kNT * 2 * 64 + lane) * 16;
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const v8h bhi = *(const v8h *)(fb + (nt * 2 + 0) * 64 * 16);
-        const v8h blo = *(const v8h *)(fb + (nt * 2 + 1) * 64 * 16);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) c[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mt], bhi, c[mt][nt], 0, 0, 0);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) c[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mt], blo, c[mt][nt], 0, 0, 0);
-      }
+    for (int pp = 0; pp < 2; ++pp) {
+      int ch = tid + 64 * kWaves * pp;
+      ch = ch < nst ? ch : nst - 1;
+      const int grp = ch / (half_m), within = ch - grp * half_m;
+      cs_lds[pp] = kCodeOff + grp * kGroupPitch + 16 * within;
+      cs_glb[pp] = 16 * ch;
     }
+  }
+  // nibble transpose within lane quads
+  const unsigned perm_sel = (lane & 2) ? 0x03070105u : 0x06020400u;
+  const unsigned rot_sh = (lane & 1) ? 4u : 28u;
+  const unsigned keep = (lane & 1) ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
 
-    // ---- 64-point Walsh-Hadamard over i.  c[mt][nt][r] holds row
-    // i = 32 mt + 8 (r >> 2) + 4 h + (r & 3): register bits r0, r1, r2, r3
-    // carry i0, i1, i3, i4; mt carries i5; lane bit 5 carries i2.
+  // DMA of X row r into LDS buffer bsel, one wave-instruction per k-step
+  // region: instruction q of this wave covers bytes 1024 (4 q + wave) ..
+  // +1023 of the row (a coalesced 1 KB).  Lanes past the row's end re-read its
+  // last 16 bytes; instructions past the last chunk repeat it (small m only).
+  int dma_src[kKS], dma_dst[kKS];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+  for (int q = 0; q < kKS; ++q) {
+    int chunk = q * kWaves + wave;
+    chunk = chunk < nchunks ? chunk : nchunks - 1;
+    dma_dst[q] = 1024 * chunk;
+    const int off = 1024 * chunk + 16 * lane;
+    dma_src[q] = off < rowb - 16 ? off : rowb - 16;
+  }
+  auto issue_dma = [&](const uint8_t *src, int bsel, int q) __attribute__((always_inline)) {
+    __builtin_amdgcn_global_load_lds((const void *)(src + dma_src[q]),
+                                     (lds_void *)(smem + bsel * kRowBuf + dma_dst[q]), 16, 0, 0);
+  };
+
+  v4f S[2][kMT][kNTW];   // two rows: one in the MFMA phase, one being finished
+  float row_max = 0.f;   // absmax of the row whose codes are staged in LDS
+
+  // One row step, all compile-time: the MFMAs of the row in LDS buffer MS
+  // into register set MS (MS < 0: none), the transform, maximum,
+  // quantization and code staging of the row in register set PS (PS < 0:
+  // none), and, if ST, the global stores of the codes staged by the
+  // previous step (row srow).
+  auto step = [&](auto ms_tag, auto ps_tag, auto st_tag, int64_t srow, const uint8_t *next_src)
+                  __attribute__((always_inline)) {
+    constexpr int MS = decltype(ms_tag)::value;
+    constexpr int PS = decltype(ps_tag)::value;
+    constexpr bool ST = decltype(st_tag)::value != 0;
+    const uint8_t *xb = smem + (MS > 0 ? kRowBuf : 0);
+    v8h acur[kMT], anxt[kMT];
+    v4h a5[kMT];
+    unsigned w[kNTW][2];
+    float mx = 0.f, inv = 0.f;
+    if constexpr (MS >= 0) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if (r & (1 << rb)) continue;
-            const float u = c[mt][nt][r], v = c[mt][nt][r | (1 << rb)];
-            c[mt][nt][r] = u + v;
-            c[mt][nt][r | (1 << rb)] = u - v;
-          }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {   // i5
-        const float u = c[0][nt][r], v = c[1][nt][r];
-        c[0][nt][r] = u + v;
-        c[1][nt][r] = u - v;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {   // i2: lane bit 5 <-> the M-tile bit, then butterfly
-        float u = c[0][nt][r], v = c[1][nt][r];
-        swap32(u, v);
-        c[0][nt][r] = u + v;
-        c[1][nt][r] = u - v;
-      }
+      for (int mt = 0; mt < kMT; ++mt) acur[mt] = __builtin_bit_cast(v8h, *(const v4u *)(xb + a_off[mt] + 16 * g));
     }
-    // Now c[q][nt][r] is output row j = (r & 3) | q << 2 | (r >> 2) << 3 | h << 5,
-    // column b = 6 ri + nt (zero for b >= m: padded O columns are zero).
-
-    float mx = 0.f;
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int ks = 0; ks < kKS; ++ks) {
+      if constexpr (MS >= 0) {
+        // the next row's X, into the other buffer (free since the top barrier)
+        issue_dma(next_src, 1 - MS, ks);
+        if (ks + 1 < kKS - 1) {
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
+          for (int mt = 0; mt < kMT; ++mt)
+            anxt[mt] = __builtin_bit_cast(v8h, *(const v4u *)(xb + a_off[mt] + 16 * g + 64 * (ks + 1)));
+        } else if (ks + 1 == kKS - 1) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(c[q][nt][r]));
-    mx = wave_max(mx);
-    if (lane == 0) scales[row] = mx * scale_mul;
-    const float inv = mx > 0.f ? 7.0f / mx : 0.f;
-
-    uint8_t *cr = codes + row * (int64_t)(n / 2);
+          for (int mt = 0; mt < kMT; ++mt)
+            a5[mt] = __builtin_bit_cast(v4h, *(const v2u *)(xb + a_off[mt] + 8 * g + 320));
+        }
+        // the twelve hi products, then the twelve lo ones: an accumulator's
+        // two updates are twelve MFMAs apart
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+        for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = (r & 3) | (q << 2) | ((r >> 2) << 3) | (h << 5);
-        uint8_t *dst = cr + (j * m + 6 * ri) / 2;
+          for (int t = 0; t < kNTW; ++t)
 #pragma unroll
-        for (int pr = 0; pr < 3; ++pr) {
-          if (6 * ri + 2 * pr < m) {
-            const unsigned b0 = round_bits(c[q][2 * pr][r], inv);
-            const unsigned b1 = round_bits(c[q][2 * pr + 1][r], inv);
-            dst[pr] = (uint8_t)((b0 & 0xFu) | ((b1 & 0xFu) << 4));
-          }
+            for (int mt = 0; mt < kMT; ++mt) {
+              if (ks == 0 && hl == 0)   // the row's first product: C = 0
+                S[MS][mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acur[mt], ob[t][ks][hl], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+              else if (ks < kKS - 1)
+                S[MS][mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acur[mt], ob[t][ks][hl], S[MS][mt][t], 0, 0, 0);
+              else
+                S[MS][mt][t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a5[mt], ob5[t][hl], S[MS][mt][t], 0, 0, 0);
+            }
+        if (ks + 1 < kKS - 1) {
+#pragma unroll
+          for (int mt = 0; mt < kMT; ++mt) acur[mt] = anxt[mt];
         }
       }
+      if constexpr (ST) {
+        if (ks == 0) {
+          uint8_t *cr = codes + srow * (int64_t)code_bytes;
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) *(v4u *)(cr + cs_glb[pp]) = *(const v4u *)(smem + cs_lds[pp]);
+          if (lane == 0) scales[srow] = row_max * scale_mul;
+        }
+      }
+      if constexpr (PS >= 0) {
+        if (ks <= 2) {
+          // 64-point Walsh-Hadamard over i for N-tile t = ks.  Element r of
+          // S[PS][mt][t] is row i = 32 (mt >> 1) + 8 g + 2 r + (mt & 1):
+          // i0 = mt bit 0, i1 = r bit 0, i2 = r bit 1, i3 = lane bit 4,
+          // i4 = lane bit 5, i5 = mt bit 1.
+          const int t = ks;
+#pragma unroll
+          for (int mb = 1; mb <= 2; mb <<= 1)
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt) {
+              if (mt & mb) continue;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float u = S[PS][mt][t][r], v = S[PS][mt | mb][t][r];
+                S[PS][mt][t][r] = u + v;
+                S[PS][mt | mb][t][r] = u - v;
+              }
+            }
+#pragma unroll
+          for (int rb = 1; rb <= 2; rb <<= 1)
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                if (r & rb) continue;
+                const float u = S[PS][mt][t][r], v = S[PS][mt][t][r | rb];
+                S[PS][mt][t][r] = u + v;
+                S[PS][mt][t][r | rb] = u - v;
+              }
+          // i3: lane bit 4 <-> M-tile bit 0 (done), then butterfly over M-tile bit 0
+#pragma unroll
+          for (int mt = 0; mt < kMT; mt += 2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float u = S[PS][mt][t][r], v = S[PS][mt + 1][t][r];
+              swap16(u, v);
+              S[PS][mt][t][r] = u + v;
+              S[PS][mt + 1][t][r] = u - v;
+            }
+          // i4: lane bit 5 <-> register bit 0 (done), then butterfly over register bit 0
+#pragma unroll
+          for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              float u = S[PS][mt][t][r], v = S[PS][mt][t][r + 1];
+              swap32(u, v);
+              S[PS][mt][t][r] = u + v;
+              S[PS][mt][t][r + 1] = u - v;
+            }
+          // Element r of S[PS][mt][t] is now output row
+          //   j = g | (r >> 1) << 2 | (mt & 1) << 3 | (r & 1) << 4 | (mt >> 1) << 5,
+          // column b = 16 (3 wave + t) + c16 (zero for b >= m: O's padding is zero).
+        }
+        if (ks == 3) {
+#pragma unroll
+          for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+            for (int t = 0; t < kNTW; ++t)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(S[PS][mt][t][r]));
+          mx = wave_max_dpp(mx);
+          if (lane == 0) wmax[wave] = mx;
+        }
+        if (ks == 4) {
+          mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+          inv = mx > 0.f ? 7.0f / mx : 0.f;
+          // four-bit two's complement codes; nibble 4 k + 16 h of w[t][R]
+          // is the code of element r of S[PS][mt][t] with
+          // k = (r >> 1) | (mt & 1) << 1, h = r & 1, R = mt >> 1.  Each
+          // alignbit shifts the word right by four and inserts the next code
+          // at the top, so codes enter in nibble order.
+#pragma unroll
+          for (int t = 0; t < kNTW; ++t)
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+              unsigned acc = 0u;
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  const int mt = 2 * R + (k >> 1), r = (k & 1) * 2 + h;
+                  acc = __builtin_amdgcn_alignbit(round_bits(S[PS][mt][t][r], inv), acc, 4);
+                }
+              w[t][R] = acc;
+            }
+          row_max = mx;
+        }
+        if (ks == 5) {
+          // 4 x 4 nibble transposes within each lane quad, exchanging the
+          // quad lane index (the column's low two bits) with k
+#pragma unroll
+          for (int t = 0; t < kNTW; ++t)
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+              unsigned v = w[t][R];
+              v = __builtin_amdgcn_perm(dpp<kQuadXor2>(v), v, perm_sel);   // lane bit 1 <-> k bit 1
+              const unsigned o = dpp<kQuadXor1>(v);                         // lane bit 0 <-> k bit 0
+              const unsigned sh = __builtin_amdgcn_alignbit(o, o, rot_sh);
+              v = (keep & v) | (~keep & sh);
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                *(unsigned short *)(smem + cw_off[t] + (2 * R + h) * kGroupPitch) = (unsigned short)(v >> (16 * h));
+            }
+        }
+        // block-wide hand-offs: the four partial maxima, then the staged codes
+        if (ks == 3 || ks == 5) {
+          wait_lgkm0();
+          __builtin_amdgcn_s_barrier();
+        }
+      }
+    }
+  };
+
+  // Rows r_k = block + k * grid: X of row r_{k+1} is in flight while row r_k
+  // is multiplied, row r_{k-1} is finished during those MFMAs, and the codes
+  // of row r_{k-2} are stored.
+  const int64_t stride = gridDim.x;
+  const int64_t row0 = blockIdx.x;   // the grid is no larger than rows
+  const int64_t nblk = (rows - row0 + stride - 1) / stride;
+  auto rowk = [&](int64_t k) { return row0 + k * stride; };
+  // (past the block's last row: that row again, into the free buffer)
+  auto row_src = [&](int64_t k) { return (const uint8_t *)(x + rowk(k < nblk ? k : nblk - 1) * ld_x); };
+  {
+    const uint8_t *src = row_src(0);
+#pragma unroll
+    for (int q = 0; q < kKS; ++q) issue_dma(src, 0, q);
   }
+  // top of row step k: row r_k has landed in every wave's part of its
+  // buffer (the stores a step issues went out thousands of cycles before)
+  auto top = [&]() __attribute__((always_inline)) {
+    wait_vm<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  };
+  top();
+  step(IC<0>{}, IC<-1>{}, IC<0>{}, 0, row_src(1));
+  if (nblk > 1) {
+    top();
+    step(IC<1>{}, IC<0>{}, IC<0>{}, 0, row_src(2));
+  }
+  if (nblk > 2) {
+    top();
+    step(IC<0>{}, IC<1>{}, IC<1>{}, rowk(0), row_src(3));
+  }
+  int64_t k = 3;
+  for (; k + 1 < nblk; k += 2) {
+    top();
+    step(IC<1>{}, IC<0>{}, IC<1>{}, rowk(k - 2), row_src(k + 1));
+    top();
+    step(IC<0>{}, IC<1>{}, IC<1>{}, rowk(k - 1), row_src(k + 2));
+  }
+  if (k < nblk) {
+    top();
+    step(IC<1>{}, IC<0>{}, IC<1>{}, rowk(k - 2), row_src(k + 1));
+  }
+  // the last row r_{n-1} is in register set (n - 1) & 1
+  if (nblk == 1)
+    step(IC<-1>{}, IC<0>{}, IC<0>{}, 0, nullptr);
+  else if ((nblk - 1) & 1)
+    step(IC<-1>{}, IC<1>{}, IC<1>{}, rowk(nblk - 2), nullptr);
+  else
+    step(IC<-1>{}, IC<0>{}, IC<1>{}, rowk(nblk - 2), nullptr);
+  step(IC<-1>{}, IC<-1>{}, IC<1>{}, rowk(nblk - 1), nullptr);
+  wait_vm<0>();   // no DMA may still be writing this block's LDS when it exits
 }
 
 }  // namespace
 
 bool rq_kron_supported(const RotArgs &r, int group) {
-  return r.dense_m > 1 && r.had_n == 64 && r.dense_m <= 16 * kMaxKS && r.dense_m % 4 == 0 &&
-         r.signs == nullptr && group == 0;
+  return r.dense_m > 1 && r.had_n == 64 && r.dense_m <= 176 && r.dense_m % 4 == 0 && r.signs == nullptr &&
+         group == 0;
 }
 
 hipError_t launch_rq_kron(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
                           uint8_t *codes, float *scales, hipStream_t stream) {
   (void)group;
-  const int KS = (r.dense_m + 15) / 16;
-  const size_t lds = (size_t)KS * kNT * 2 * 64 * 16;
-  hipError_t e = hipFuncSetAttribute((const void *)rq_kron_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
-  if (e != hipSuccess) return e;
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int64_t blocks = (rows + kWaves - 1) / kWaves;
-  const int64_t grid = blocks < cus ? blocks : cus;
+  const int64_t grid = rows < cus ? rows : cus;
   const float scale_mul = (float)(1.0 / (7.0 * 8.0));   // 1/(7 sqrt(64))
-  rq_kron_kernel<<<dim3((unsigned)grid), dim3(64 * kWaves), lds, stream>>>(
+  rq_kron_kernel<<<dim3((unsigned)grid), dim3(64 * kWaves), 0, stream>>>(
       (const unsigned short *)x, rows, ld_x, r.dense_m, r.dense, codes, scales, scale_mul);
   return hipGetLastError();
 }

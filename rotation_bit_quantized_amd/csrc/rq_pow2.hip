@@ -67,6 +67,35 @@ constexpr int lds_bytes() {
   return kWaves * kBufs * (2 << L);
 }
 
+// The B operands (the +-1 64-point factor, columns permuted) of every lane,
+// computed at compile time: entry [s][nt][lane] is the v8h for k-step s and
+// N-tile nt; slot j holds (-1)^parity with parity = popcount((j & 3) & nt) +
+// popcount(g & (c16 & 3)) + ((j >> 2) & (c16 >> 2) & 1) + (s & (c16 >> 3)).
+struct BopTable {
+  unsigned w[2][4][64][4];
+};
+constexpr BopTable make_bop_table() {
+  BopTable t{};
+  for (int s = 0; s < 2; ++s)
+    for (int nt = 0; nt < 4; ++nt)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int c16 = lane & 15, g = lane >> 4;
+        for (int d = 0; d < 4; ++d) {
+          unsigned word = 0;
+          for (int half = 0; half < 2; ++half) {
+            const int j = 2 * d + half;
+            int par = ((j & 3) & nt) ^ (g & (c16 & 3));
+            par = (par & 1) ^ ((par >> 1) & 1);
+            par ^= ((j >> 2) & (c16 >> 2) & 1) ^ (s & (c16 >> 3));
+            word |= (par ? 0xBC00u : 0x3C00u) << (16 * half);
+          }
+          t.w[s][nt][lane][d] = word;
+        }
+      }
+  return t;
+}
+__device__ constexpr BopTable kBop = make_bop_table();
+
 // Register index of a value: bits 0-1 = r (MFMA output row within the 4-row
 // group), bits 2-3 = N-tile, bits 4.. = M-tile.
 template <int L, int GROUP>
@@ -99,13 +128,7 @@ __global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int par = __builtin_popcount((j & 3) & nt) + __builtin_popcount(g & (c16 & 3)) +
-                        ((j >> 2) & (c16 >> 2) & 1) + (s & (c16 >> 3));
-        bop[s][nt][j] = (par & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
-      }
+    for (int nt = 0; nt < 4; ++nt) bop[s][nt] = __builtin_bit_cast(v8h, *(const v4u *)kBop.w[s][nt][lane]);
 
   const int64_t wave_id = (int64_t)blockIdx.x * kWaves + wave;
   const int64_t wave_stride = (int64_t)gridDim.x * kWaves;

@@ -151,9 +151,11 @@ def test_rq_kron_small_dense(qr):
         check_rq(qr, x, had_n * m, had_n, dense=o, signs=signs)
 
 
-@pytest.mark.parametrize("m,rows", [(172, 5), (176, 64), (8, 33), (100, 130), (4, 3)])
+@pytest.mark.parametrize("m,rows", [(172, 5), (176, 64), (8, 33), (100, 130), (4, 3),
+                                    (8, 3000), (100, 1000), (172, 600)])
 def test_rq_kron_fast_path(qr, m, rows):
-    """64 x m Kronecker rotations without signs (the MFMA Kronecker kernel)."""
+    """64 x m Kronecker rotations without signs (the MFMA Kronecker kernel);
+    the larger row counts give each persistent block several rows."""
     o = np.linalg.qr(np.random.default_rng(m).standard_normal((m, m)))[0].astype(np.float32)
     x = W.make_random_rows(rows, 64 * m, seed=m + rows, scale=2.0)
     x[:, 3] *= 50
