@@ -14,17 +14,18 @@
 //
 // Design (one token row at a time per block of four waves, persistent grid,
 // one block per CU):
-//  * The dense product runs on v_mfma_f32_16x16x32_f16 (the last 16 of K on
-//    v_mfma_f32_16x16x16_f16) with A = X (the fp16 input, exact) and B = O
+//  * The dense product runs on v_mfma_f32_16x16x32_f16 with A = X (the fp16
+//    input, exact) and B = O
 //    split into an fp16 high part and an fp16 low part (O - hi); both
 //    products accumulate into the same fp32 accumulators (error near 2^-22
 //    relative; one fp16 pass alone would round O to 2^-11 and move codes that
-//    sit near a rounding boundary).  K (a) is padded to 176, N (b) to 192.
+//    sit near a rounding boundary).  K (a) and N (b) are padded to 192.
 //  * O's B-fragments stay in AGPRs for the whole kernel, split over the
-//    waves: wave w owns N-tiles 3w .. 3w+2 (132 registers of hi/lo parts).
+//    waves: wave w owns N-tiles 3w .. 3w+2 (144 registers of hi/lo parts).
 //  * The X row travels by coalesced global_load_lds DMA (1 KB per wave
-//    instruction, one per k-step) into one of two LDS buffers shared by the
-//    four waves, a row ahead.  M-tile mt holds the rows
+//    instruction, one per k-step) into one of three LDS buffers shared by
+//    the four waves, two rows ahead (HBM latency stays hidden although the
+//    DMA is spread over a whole row step).  M-tile mt holds the rows
 //    i = 32 (mt >> 1) + 2 c + (mt & 1), c < 16: with the 344-byte row pitch
 //    of m = 172, sixteen such rows start in sixteen distinct bank groups.
 //  * Software pipeline over rows with two accumulator sets in VGPRs: while
@@ -54,14 +55,18 @@ using IC = std::integral_constant<int, V>;
 
 constexpr int kWaves = 4;
 constexpr int kMT = 4;          // M-tiles of 16 rows i
-constexpr int kKS = 6;          // five k-steps of 32 (a < 160) and one of 16 (a < 176)
+constexpr int kKS = 6;          // k-steps of 32: a < 192
 constexpr int kNTW = 3;         // N-tiles of 16 per wave: b < 192
 constexpr int kRowBuf = 23552;  // one X row (<= 22528 bytes) plus the A-read overrun past it
 constexpr int kGroupPitch = 1408;                // LDS bytes per 16 output rows j of codes (16 * 176 / 2)
-constexpr int kCodeOff = 2 * kRowBuf;            // codes of one row, four groups of 16 rows j
+constexpr int kRowBufs = 3;                      // X rows r_k, r_{k+1} resident, r_{k+2} landing
+// The codes, a sink and the maxima live in an LDS array of their own: the
+// compiler can then tell that their reads do not alias the X rows' DMA
+// (otherwise it waits for that DMA before each such read).
+constexpr int kCodeOff = 0;                          // codes of one row, four groups of 16 rows j
 constexpr int kSinkOff = kCodeOff + 4 * kGroupPitch;   // masked-off code writes land here
 constexpr int kMaxOff = kSinkOff + 4 * kGroupPitch;    // the four waves' maxima
-constexpr int kLds = kMaxOff + 16;
+constexpr int kAux = kMaxOff + 16;
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -110,8 +115,9 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
     const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, int m, const float *__restrict__ dense,
     uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
-  float *const wmax = (float *)(smem + kMaxOff);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kRowBufs * kRowBuf];   // X rows
+  __shared__ __attribute__((aligned(16))) uint8_t aux[kAux];
+  float *const wmax = (float *)(aux + kMaxOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,12 +129,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
   const int code_bytes = 32 * m;            // n / 2
   const int half_m = m >> 1;
 
-  // ---- this wave's B-fragments of O, fp16 hi and lo parts.  32-wide
-  // k-steps: lane (c16, g) holds O[32 ks + 8 g + j][b], j < 8; the 16-wide
-  // last one O[160 + 4 g + j][b], j < 4; b = 16 (3 wave + t) + c16; zero
+  // ---- this wave's B-fragments of O, fp16 hi and lo parts: lane (c16, g)
+  // holds O[32 ks + 8 g + j][b], j < 8, b = 16 (3 wave + t) + c16; zero
   // past m.
-  v8h ob[kNTW][kKS - 1][2];
-  v4h ob5[kNTW][2];
+  v8h ob[kNTW][kKS][2];
   auto o_at = [&](int a, int b) __attribute__((always_inline)) {
     const bool in = a < m && b < m;
     const float o = dense[in ? a * m + b : 0];   // clamped load, then select
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
   for (int t = 0; t < kNTW; ++t) {
     const int b = 16 * (kNTW * wave + t) + c16;
 #pragma unroll
-    for (int ks = 0; ks < kKS - 1; ++ks)
+    for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float o = o_at(32 * ks + 8 * g + j, b);
@@ -146,13 +150,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
         ob[t][ks][0][j] = h;
         ob[t][ks][1][j] = (_Float16)(o - (float)h);
       }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float o = o_at(160 + 4 * g + j, b);
-      const _Float16 h = (_Float16)o;
-      ob5[t][0][j] = h;
-      ob5[t][1][j] = (_Float16)(o - (float)h);
-    }
   }
 
   // O lives in AGPRs (MFMA reads its B operand from there); the VGPRs hold
@@ -161,17 +158,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
 #pragma unroll
   for (int t = 0; t < kNTW; ++t) {
 #pragma unroll
-    for (int ks = 0; ks < kKS - 1; ++ks)
+    for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
       for (int hl = 0; hl < 2; ++hl) asm volatile("" : "+a"(ob[t][ks][hl]));
-#pragma unroll
-    for (int hl = 0; hl < 2; ++hl) asm volatile("" : "+a"(ob5[t][hl]));
   }
   // A reads that run past a row's DMA'd bytes (small m) must see finite
   // values (they meet zero columns of O): clear each buffer's tail once.
   for (int off = rowb + 16 * tid; off + 16 <= kRowBuf; off += 16 * 64 * kWaves) {
-    *(v4u *)(smem + off) = v4u{0u, 0u, 0u, 0u};
-    *(v4u *)(smem + kRowBuf + off) = v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b = 0; b < kRowBufs; ++b) *(v4u *)(smem + b * kRowBuf + off) = v4u{0u, 0u, 0u, 0u};
   }
 
   // ---- per-lane constants
@@ -189,17 +184,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
 #pragma unroll
   for (int t = 0; t < kNTW; ++t) {
     const int col = 16 * (kNTW * wave + t) + 4 * (c16 >> 2);
-    cw_off[t] = col < m ? kCodeOff + (g | ((c16 & 3) << 2)) * half_m + (col >> 1) : kSinkOff;
+    // (columns past m: a sink address of the lane's own, so such writes
+    // do not pile up on one LDS address)
+    cw_off[t] = col < m ? kCodeOff + (g | ((c16 & 3) << 2)) * half_m + (col >> 1) : kSinkOff + 2 * lane;
   }
-  // code stores: 16-byte chunks ch = tid, tid + 256 of the row (clamped
-  // duplicates past its end); a chunk never straddles a group (8 m bytes).
+  // code stores: 16-byte chunks ch = tid, tid + 256 of the row; a lane past
+  // the row's end stores chunk ch mod nst again (the same bytes, at
+  // distinct addresses: no branch, no pile-up on one address); a chunk never
+  // straddles a group (8 m bytes).
   int cs_lds[2], cs_glb[2];
   {
     const int nst = code_bytes / 16;
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       int ch = tid + 64 * kWaves * pp;
-      ch = ch < nst ? ch : nst - 1;
+      ch = ch < nst ? ch : ch % nst;
       const int grp = ch / (half_m), within = ch - grp * half_m;
       cs_lds[pp] = kCodeOff + grp * kGroupPitch + 16 * within;
       cs_glb[pp] = 16 * ch;
@@ -223,46 +222,56 @@ __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
     const int off = 1024 * chunk + 16 * lane;
     dma_src[q] = off < rowb - 16 ? off : rowb - 16;
   }
+  // Issued from inline assembly: the compiler then does not see an LDS
+  // write it would wait for (it cannot tell the A-fragment reads of other
+  // buffers apart and would wait for the whole DMA before each); the
+  // explicit vmcnt waits below order every use.  The DMA writes no
+  // register (the scratch SGPR holds m0 across it).
+  const unsigned smem_lds = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)smem;
   auto issue_dma = [&](const uint8_t *src, int bsel, int q) __attribute__((always_inline)) {
-    __builtin_amdgcn_global_load_lds((const void *)(src + dma_src[q]),
-                                     (lds_void *)(smem + bsel * kRowBuf + dma_dst[q]), 16, 0, 0);
+    const unsigned dst = __builtin_amdgcn_readfirstlane(smem_lds + (unsigned)(bsel * kRowBuf + dma_dst[q]));
+    unsigned saved;   // m0 is reserved to the compiler: restore it
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src + dma_src[q]), "s"(dst)
+        : "memory");
   };
 
   v4f S[2][kMT][kNTW];   // two rows: one in the MFMA phase, one being finished
-  float row_max = 0.f;   // absmax of the row whose codes are staged in LDS
+  v8h apre[kMT];         // the next row's k-step 0 A-fragments, read a region ahead
 
-  // One row step, all compile-time: the MFMAs of the row in LDS buffer MS
-  // into register set MS (MS < 0: none), the transform, maximum,
-  // quantization and code staging of the row in register set PS (PS < 0:
-  // none), and, if ST, the global stores of the codes staged by the
-  // previous step (row srow).
-  auto step = [&](auto ms_tag, auto ps_tag, auto st_tag, int64_t srow, const uint8_t *next_src)
+  // One row step k, all compile-time flags: the MFMAs of row r_k (in LDS
+  // buffer k % 3) into register set MS (MS < 0: none), and the transform,
+  // maximum, quantization, code staging and stores of row prow in register
+  // set PS (PS < 0: none).  Six k-step regions; the MFMAs of each are
+  // interleaved with one part of the other row's work:
+  //   0-2: transform of N-tile t = ks   3: absmax, then barrier
+  //   4: quantize, transpose, stage codes; DMA wait for r_{k+1}; barrier
+  //   5: store prow's codes; read r_{k+1}'s k-step 0 A-fragments
+  auto step = [&](auto ms_tag, auto ps_tag, int xbuf, int nbuf, int dbuf, uint8_t *cr, float *sp,
+                  const uint8_t *next_src)
                   __attribute__((always_inline)) {
     constexpr int MS = decltype(ms_tag)::value;
     constexpr int PS = decltype(ps_tag)::value;
-    constexpr bool ST = decltype(st_tag)::value != 0;
-    const uint8_t *xb = smem + (MS > 0 ? kRowBuf : 0);
+    // r_k is in buffer k % 3; r_{k+2} goes to (k + 2) % 3, which r_{k-1}
+    // left at the previous step's k-step 4 barrier
+    const uint8_t *xb = smem + xbuf * kRowBuf;
     v8h acur[kMT], anxt[kMT];
-    v4h a5[kMT];
     unsigned w[kNTW][2];
     float mx = 0.f, inv = 0.f;
     if constexpr (MS >= 0) {
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) acur[mt] = __builtin_bit_cast(v8h, *(const v4u *)(xb + a_off[mt] + 16 * g));
+      for (int mt = 0; mt < kMT; ++mt) acur[mt] = apre[mt];
     }
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       if constexpr (MS >= 0) {
-        // the next row's X, into the other buffer (free since the top barrier)
-        issue_dma(next_src, 1 - MS, ks);
-        if (ks + 1 < kKS - 1) {
+        issue_dma(next_src, dbuf, ks);
+        if (ks + 1 < kKS) {
 #pragma unroll
           for (int mt = 0; mt < kMT; ++mt)
             anxt[mt] = __builtin_bit_cast(v8h, *(const v4u *)(xb + a_off[mt] + 16 * g + 64 * (ks + 1)));
-        } else if (ks + 1 == kKS - 1) {
-#pragma unroll
-          for (int mt = 0; mt < kMT; ++mt)
-            a5[mt] = __builtin_bit_cast(v4h, *(const v2u *)(xb + a_off[mt] + 8 * g + 320));
         }
         // the twelve hi products, then the twelve lo ones: an accumulator's
         // two updates are twelve MFMAs apart
@@ -274,22 +283,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
             for (int mt = 0; mt < kMT; ++mt) {
               if (ks == 0 && hl == 0)   // the row's first product: C = 0
                 S[MS][mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acur[mt], ob[t][ks][hl], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-              else if (ks < kKS - 1)
-                S[MS][mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acur[mt], ob[t][ks][hl], S[MS][mt][t], 0, 0, 0);
               else
-                S[MS][mt][t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a5[mt], ob5[t][hl], S[MS][mt][t], 0, 0, 0);
+                S[MS][mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acur[mt], ob[t][ks][hl], S[MS][mt][t], 0, 0, 0);
             }
-        if (ks + 1 < kKS - 1) {
+        if (ks + 1 < kKS) {
 #pragma unroll
           for (int mt = 0; mt < kMT; ++mt) acur[mt] = anxt[mt];
         }
-      }
-      if constexpr (ST) {
-        if (ks == 0) {
-          uint8_t *cr = codes + srow * (int64_t)code_bytes;
+        if (ks == kKS - 1) {
+          // r_{k+1} is in every wave's part of buffer nbuf since the k-step 4 barrier
 #pragma unroll
-          for (int pp = 0; pp < 2; ++pp) *(v4u *)(cr + cs_glb[pp]) = *(const v4u *)(smem + cs_lds[pp]);
-          if (lane == 0) scales[srow] = row_max * scale_mul;
+          for (int mt = 0; mt < kMT; ++mt)
+            apre[mt] = __builtin_bit_cast(v8h, *(const v4u *)(smem + nbuf * kRowBuf + a_off[mt] + 16 * g));
         }
       }
       if constexpr (PS >= 0) {
@@ -372,15 +377,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
 #pragma unroll
               for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                  const int mt = 2 * R + (k >> 1), r = (k & 1) * 2 + h;
+                for (int kk = 0; kk < 4; ++kk) {
+                  const int mt = 2 * R + (kk >> 1), r = (kk & 1) * 2 + h;
                   acc = __builtin_amdgcn_alignbit(round_bits(S[PS][mt][t][r], inv), acc, 4);
                 }
               w[t][R] = acc;
             }
-          row_max = mx;
-        }
-        if (ks == 5) {
           // 4 x 4 nibble transposes within each lane quad, exchanging the
           // quad lane index (the column's low two bits) with k
 #pragma unroll
@@ -394,68 +396,97 @@ __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
               v = (keep & v) | (~keep & sh);
 #pragma unroll
               for (int h = 0; h < 2; ++h)
-                *(unsigned short *)(smem + cw_off[t] + (2 * R + h) * kGroupPitch) = (unsigned short)(v >> (16 * h));
+                *(unsigned short *)(aux + cw_off[t] + (2 * R + h) * kGroupPitch) = (unsigned short)(v >> (16 * h));
             }
         }
-        // block-wide hand-offs: the four partial maxima, then the staged codes
-        if (ks == 3 || ks == 5) {
-          wait_lgkm0();
-          __builtin_amdgcn_s_barrier();
+        if (ks == 5) {
+          // the block stores the row's codes as 16-byte chunks, one lane the scale
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const v4u v = *(const v4u *)(aux + cs_lds[pp]);
+            *(v4u *)(cr + cs_glb[pp]) = v;
+          }
+          if (tid == 0) *sp = mx * scale_mul;
         }
       }
+      // block-wide hand-offs: the four partial maxima (k-step 3); the staged
+      // codes and r_{k+1}'s row (k-step 4).  r_{k+1}'s DMA was issued during
+      // the previous step; this step has issued five DMA instructions since
+      // (and the previous step's stores went out before them): with
+      // in-order completion, at most five outstanding operations means
+      // r_{k+1} is in.
+      if (ks == 3 && PS >= 0) {
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+      }
+      if (ks == 4 && (MS >= 0 || PS >= 0)) {
+        if (MS >= 0) wait_vm<kKS - 1>();
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+      }
+      // region fence: the A reads a region issues for the next one stay a
+      // whole region of MFMAs ahead of their first use
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Rows r_k = block + k * grid: X of row r_{k+1} is in flight while row r_k
-  // is multiplied, row r_{k-1} is finished during those MFMAs, and the codes
-  // of row r_{k-2} are stored.
-  const int64_t stride = gridDim.x;
+  // Rows r_k = block + k * grid: X of row r_{k+2} is in flight while row r_k
+  // is multiplied, and row r_{k-1} is finished and stored during those
+  // MFMAs.
+  // Per-step bookkeeping is scalar and cheap: rotating buffer indices and
+  // running row pointers.
+  const int stride = (int)gridDim.x;
   const int64_t row0 = blockIdx.x;   // the grid is no larger than rows
-  const int64_t nblk = (rows - row0 + stride - 1) / stride;
-  auto rowk = [&](int64_t k) { return row0 + k * stride; };
-  // (past the block's last row: that row again, into the free buffer)
-  auto row_src = [&](int64_t k) { return (const uint8_t *)(x + rowk(k < nblk ? k : nblk - 1) * ld_x); };
-  {
-    const uint8_t *src = row_src(0);
+  // rows of this block, wave-uniform in an SGPR
+  const int nblk = __builtin_amdgcn_readfirstlane((int)((rows - row0 + stride - 1) / stride));
+  const int64_t x_step = (int64_t)stride * ld_x * 2;   // bytes between a block's rows
+  const uint8_t *const x0 = (const uint8_t *)(x + row0 * ld_x);
+  const uint8_t *const x_last = x0 + (int64_t)(nblk - 1) * x_step;
+  // (past the block's last row: that row again, into a free buffer)
+  auto clamp_src = [&](int kk, const uint8_t *p) { return kk < nblk ? p : x_last; };
+  auto rot = [](int b) { return b == kRowBufs - 1 ? 0 : b + 1; };
 #pragma unroll
-    for (int q = 0; q < kKS; ++q) issue_dma(src, 0, q);
+  for (int b = 0; b < 2; ++b) {
+    const uint8_t *src = clamp_src(b, x0 + b * x_step);
+#pragma unroll
+    for (int q = 0; q < kKS; ++q) issue_dma(src, b, q);
   }
-  // top of row step k: row r_k has landed in every wave's part of its
-  // buffer (the stores a step issues went out thousands of cycles before)
-  auto top = [&]() __attribute__((always_inline)) {
-    wait_vm<0>();
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
+  wait_vm<kKS>();   // r_0 is in (r_1's six instructions may be outstanding)
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) apre[mt] = __builtin_bit_cast(v8h, *(const v4u *)(smem + a_off[mt] + 16 * g));
+  const uint8_t *src2 = x0 + 2 * x_step;               // row r_{k+2}
+  uint8_t *crow = codes + row0 * (int64_t)code_bytes;  // codes of row r_{k-1}
+  float *srow = scales + row0;
+  const int64_t c_step = (int64_t)stride * code_bytes;
+  step(IC<0>{}, IC<-1>{}, 0, 1, 2, crow, srow, clamp_src(2, src2));
+  src2 += x_step;
+  int k = 1, xb = 1, nb = 2, db = 0;
+  auto advance = [&]() __attribute__((always_inline)) {
+    src2 += x_step;
+    crow += c_step;
+    srow += stride;
+    xb = rot(xb);
+    nb = rot(nb);
+    db = rot(db);
   };
-  top();
-  step(IC<0>{}, IC<-1>{}, IC<0>{}, 0, row_src(1));
-  if (nblk > 1) {
-    top();
-    step(IC<1>{}, IC<0>{}, IC<0>{}, 0, row_src(2));
-  }
-  if (nblk > 2) {
-    top();
-    step(IC<0>{}, IC<1>{}, IC<1>{}, rowk(0), row_src(3));
-  }
-  int64_t k = 3;
   for (; k + 1 < nblk; k += 2) {
-    top();
-    step(IC<1>{}, IC<0>{}, IC<1>{}, rowk(k - 2), row_src(k + 1));
-    top();
-    step(IC<0>{}, IC<1>{}, IC<1>{}, rowk(k - 1), row_src(k + 2));
+    step(IC<1>{}, IC<0>{}, xb, nb, db, crow, srow, clamp_src(k + 2, src2));
+    advance();
+    step(IC<0>{}, IC<1>{}, xb, nb, db, crow, srow, clamp_src(k + 3, src2));
+    advance();
   }
   if (k < nblk) {
-    top();
-    step(IC<1>{}, IC<0>{}, IC<1>{}, rowk(k - 2), row_src(k + 1));
+    step(IC<1>{}, IC<0>{}, xb, nb, db, crow, srow, clamp_src(k + 2, src2));
+    advance();
+    ++k;
   }
   // the last row r_{n-1} is in register set (n - 1) & 1
-  if (nblk == 1)
-    step(IC<-1>{}, IC<0>{}, IC<0>{}, 0, nullptr);
-  else if ((nblk - 1) & 1)
-    step(IC<-1>{}, IC<1>{}, IC<1>{}, rowk(nblk - 2), nullptr);
+  if ((nblk - 1) & 1)
+    step(IC<-1>{}, IC<1>{}, 0, 0, 0, crow, srow, nullptr);
   else
-    step(IC<-1>{}, IC<0>{}, IC<1>{}, rowk(nblk - 2), nullptr);
-  step(IC<-1>{}, IC<-1>{}, IC<1>{}, rowk(nblk - 1), nullptr);
+    step(IC<-1>{}, IC<0>{}, 0, 0, 0, crow, srow, nullptr);
   wait_vm<0>();   // no DMA may still be writing this block's LDS when it exits
 }
 
