@@ -186,6 +186,23 @@ def time_launches(fn, n, warm=3):
     return a.elapsed_time(b) / n
 
 
+def time_each(fn, n, stream, warm=3):
+    """Average duration (ms) of one launch of fn(i): a HIP event pair on the
+    launch stream around each of n launches (the per-dispatch span, as a
+    kernel trace reports it; gaps between launches are not counted)."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / n
+
+
 def suite(args):
     """Kernel-level throughput at each config's shape.  Buffers are cycled so
     the data touched per launch comes from HBM, not the 256 MB cache, unless
@@ -368,13 +385,12 @@ def main():
     gpu_ms = start.elapsed_time(end)
     ms_per_step = gpu_ms / args.steps
 
-    # per-kernel durations (after the timed region): back-to-back launches of
-    # each kernel on the same stream and the rotating buffer sets, HIP events
-    # around the whole sequence
+    # per-kernel durations (after the timed region, same stream, the rotating
+    # buffer sets): a HIP event pair around each launch
     nrep = max(10, args.steps)
-    rq_ms = time_launches(lambda i: rq(sets[i % nsets]), nrep)
-    gemm_ms = time_launches(lambda i: gemm(sets[i % nsets]), nrep)
-    kv_ms = time_launches(lambda i: kv(sets[i % nsets]), nrep)
+    rq_ms = time_each(lambda i: rq(sets[i % nsets]), nrep, stream)
+    gemm_ms = time_each(lambda i: gemm(sets[i % nsets]), nrep, stream)
+    kv_ms = time_each(lambda i: kv(sets[i % nsets]), nrep, stream)
 
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
