@@ -11,13 +11,18 @@
 //   step = (hi - lo) / (15 sqrt(128)), z = rint(-lo * 15/(hi - lo)),
 //   q = clamp(rint(u * 15/(hi - lo)) + z, 0, 15)
 //
-// The whole 128-point transform is one pass of v_mfma_f32_16x16x32_f16
-// (input fp16 is exact, H entries +-1 are exact, sums in fp32), computed
-// transposed: A = H_128 with its rows (the output index) permuted, held in
-// registers; B = 16 vectors of the tile as columns (one 16-byte load per lane
-// per k-step); C[output][vector].  With the permutation, lane (c16, g) holds
-// outputs 32 g .. 32 g + 31 of vector c16: the range reduction needs two
-// cross-lane steps, and the 32 codes leave as one 16-byte store.
+// The 128-point transform splits as H_128 = H_4 kron H_32 over the element
+// index k = 32 s + r and the output index jj = 32 q + p (Sylvester order:
+// H[k][jj] = H_4[s][q] H_32[r][p]).  For each 32-element slice s, one pass of
+// v_mfma_f32_16x16x32_f16 per 16 outputs computes Y_s = H_32^T X_s (A = H_32
+// with its columns permuted, +-1 in fp16, exact; B = 16 vectors of the tile
+// as columns, one 16-byte load per lane; sums in fp32), and two butterfly
+// stages over s in registers give the four q blocks.  8 MFMAs per 16 vectors,
+// and the A operand is 8 registers, so several waves per SIMD stream tiles.
+// With the permutation p = 8 (row >> 2) + 4 mt + (row & 3), lane (c16, g)
+// ends with outputs 32 q + 8 g + 0..7 of vector c16; a 4 x 4 transpose of
+// (lane bits 4, 5) x q with permlane swaps gives it codes 32 g .. 32 g + 31,
+// one 16-byte store.
 #include "qr_common.h"
 #include "qr_launch.h"
 
@@ -26,40 +31,33 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-// The A operands (permuted H_128) of every lane, computed at compile time:
-// entry [mt][s][lane] is the v8h of M-tile mt, k-step s for lane (c16, g):
-// slot j holds H[32 s + 8 g + j][32 (c16 >> 2) + 4 mt + (c16 & 3)] as fp16
-// +-1 (0x3C00 / 0xBC00), two per 32-bit word.  Loading it (32 KB, coalesced,
-// cache resident after the first waves) replaces ~1500 VALU ops per wave of
-// operand construction, which matter when a wave has only a few tiles.
-struct HopTable {
-  unsigned w[8][4][64][4];
-};
-constexpr HopTable make_hop_table() {
-  HopTable t{};
-  for (int mt = 0; mt < 8; ++mt)
-    for (int s = 0; s < 4; ++s)
-      for (int lane = 0; lane < 64; ++lane) {
-        const int c16 = lane & 15, g = lane >> 4;
-        const int jj = 32 * (c16 >> 2) + 4 * mt + (c16 & 3);
-        for (int d = 0; d < 4; ++d) {
-          unsigned word = 0;
-          for (int half = 0; half < 2; ++half) {
-            const int k = 32 * s + 8 * g + 2 * d + half;
-            int bits = k & jj, par = 0;
-            while (bits) {
-              par ^= bits & 1;
-              bits >>= 1;
-            }
-            word |= (par ? 0xBC00u : 0x3C00u) << (16 * half);
-          }
-          t.w[mt][s][lane][d] = word;
-        }
-      }
-  return t;
+__device__ __forceinline__ void swap16u(unsigned &a, unsigned &b) {
+  auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
 }
-__device__ constexpr HopTable kHop = make_hop_table();
+__device__ __forceinline__ void swap32u(unsigned &a, unsigned &b) {
+  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+// max / min over the four lanes c16 + 16 g (lane bits 4 and 5)
+__device__ __forceinline__ float max_g(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  v = fmaxf(u2f(a[0]), u2f(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  return fmaxf(u2f(b[0]), u2f(b[1]));
+}
+__device__ __forceinline__ float min_g(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  v = fminf(u2f(a[0]), u2f(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  return fminf(u2f(b[0]), u2f(b[1]));
+}
 
+// SIGNS: a sign vector is applied (its XOR masks take 16 registers, which
+// the unsigned variant spends on occupancy instead).
+template <bool SIGNS>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
     const unsigned short *__restrict__ kv, int64_t T, int H, int64_t ld_kv, const int8_t *__restrict__ signs,
     uint8_t *__restrict__ codes, float *__restrict__ scales, uint8_t *__restrict__ zeros, float step_mul) {
@@ -67,18 +65,18 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
   const int c16 = lane & 15;
   const int g = lane >> 4;
 
-  // A[mt][s]: this lane's row c16 of M-tile mt is output
-  // jj = 32 (c16 >> 2) + 4 mt + (c16 & 3); slot j holds H[k][jj] for
-  // k = 32 s + 8 g + j.  (C row 4 g' + r of M-tile mt is then output
-  // 32 g' + 4 mt + r.)
-  v8h hop[8][4];
+  // A[mt]: lane (c16, g) holds H_32[8 g + j][p] for j < 8 with
+  // p = 8 (c16 >> 2) + 4 mt + (c16 & 3): +-1 as fp16, two per word.
+  v8h hop[2];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int mt = 0; mt < 2; ++mt) {
+    const int pcol = 8 * (c16 >> 2) + 4 * mt + (c16 & 3);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) hop[mt][s] = __builtin_bit_cast(v8h, *(const v4u *)kHop.w[mt][s][lane]);
+    for (int j = 0; j < 8; ++j) hop[mt][j] = (__builtin_popcount((8 * g + j) & pcol) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+  }
   // sign masks for this lane's k-range 32 s + 8 g + 0..7 (two aligned words)
   unsigned smask[4][4];
-  if (signs != nullptr) {
+  if constexpr (SIGNS) {
     unsigned sw[4][2];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -102,8 +100,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
   const unsigned magic = f2u(kRoundMagic);
 
   // B: this lane loads vector c16 of a tile, elements 32 s + 8 g .. + 7.
-  // The next tile's loads are issued before this tile is computed, so a
-  // wave always has a tile in flight.
+  // The loads of the wave's next two tiles are in flight while a tile is
+  // computed.
   auto load_tile = [&](int64_t tile, v4u (&raw)[4]) {
     const int64_t v = tile * 16 + c16;
     const bool valid = v < nvec;
@@ -114,85 +112,116 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
     for (int s = 0; s < 4; ++s)
       raw[s] = valid ? __builtin_nontemporal_load((const v4u *)(src + 32 * s)) : v4u{0u, 0u, 0u, 0u};
   };
-  v4u raw[4];
+  v4u raw[4], nxt[4];
   if (wave_id < ntiles) load_tile(wave_id, raw);
+  if (wave_id + wave_stride < ntiles) load_tile(wave_id + wave_stride, nxt);
 
   for (int64_t tile = wave_id; tile < ntiles; tile += wave_stride) {
-    v4u nxt[4];
-    if (tile + wave_stride < ntiles) load_tile(tile + wave_stride, nxt);
+    v4u nxt2[4];
+    if (tile + 2 * wave_stride < ntiles) load_tile(tile + 2 * wave_stride, nxt2);
 
-    v4f c[8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) c[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    // Y_s for the two 16-output halves mt of p, then H_4 over s:
+    // c[q][mt][r] = output 32 q + 8 g + 4 mt + r of vector c16
+    v4f c[4][2];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       v4u w = raw[s];
-      w[0] ^= smask[s][0];
-      w[1] ^= smask[s][1];
-      w[2] ^= smask[s][2];
-      w[3] ^= smask[s][3];
+      if constexpr (SIGNS) {
+        w[0] ^= smask[s][0];
+        w[1] ^= smask[s][1];
+        w[2] ^= smask[s][2];
+        w[3] ^= smask[s][3];
+      }
       const v8h b = __builtin_bit_cast(v8h, w);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) c[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hop[mt][s], b, c[mt], 0, 0, 0);
+      for (int mt = 0; mt < 2; ++mt)
+        c[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hop[mt], b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     }
+#pragma unroll
+    for (int sb = 1; sb <= 2; sb <<= 1)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s & sb) continue;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float u = c[s][mt][r], v = c[s | sb][mt][r];
+            c[s][mt][r] = u + v;
+            c[s | sb][mt][r] = u - v;
+          }
+      }
 
-    // c[mt][r] = output 32 g + 4 mt + r of vector c16.  Range widened to
-    // include 0, over the lane's 32 outputs, then over the 4 lanes g.
+    // Range widened to include 0, over the lane's 32 outputs, then over the
+    // four lanes g of the vector.
     float mn = 0.f, mx = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        mn = fminf(mn, c[mt][r]);
-        mx = fmaxf(mx, c[mt][r]);
-      }
-    mn = fminf(mn, __shfl_xor(mn, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mn = fminf(mn, __shfl_xor(mn, 32, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          mn = fminf(mn, c[q][mt][r]);
+          mx = fmaxf(mx, c[q][mt][r]);
+        }
+    mn = min_g(mn);
+    mx = max_g(mx);
     const float rng = mx - mn;
     const float inv = rng > 0.f ? 15.0f / rng : 0.f;
     const int z = rng > 0.f ? (int)rintf(-mn * inv) : 0;
     const unsigned bias = magic - (unsigned)z;  // bits(fma) - bias = rint(u*inv) + z
+    // word[q]: codes of outputs 32 q + 8 g + 0..7 (element 0 in the low nibble)
     unsigned word[4];
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
+    for (int q = 0; q < 4; ++q) {
       unsigned acc = 0;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {   // output 32 g + 8 wd + t = mt 2 wd + t/4, r t%4
-        int q = (int)(round_bits(c[2 * wd + (t >> 2)][t & 3], inv) - bias);
-        q = min(15, max(0, q));
-        acc |= (unsigned)q << (4 * t);
+      for (int t = 0; t < 8; ++t) {
+        int qq = (int)(round_bits(c[q][t >> 2][t & 3], inv) - bias);
+        qq = min(15, max(0, qq));
+        acc |= (unsigned)qq << (4 * t);
       }
-      word[wd] = acc;
+      word[q] = acc;
     }
+    // 4 x 4 transpose of (lane bits 4, 5) x q: afterwards word[i] of lane g
+    // holds the codes of outputs 32 g + 8 i + 0..7
+    swap16u(word[0], word[1]);
+    swap16u(word[2], word[3]);
+    swap32u(word[0], word[2]);
+    swap32u(word[1], word[3]);
     const int64_t vo = tile * 16 + c16;
     if (vo < nvec) {
-      *(v4u *)(codes + vo * 64 + 16 * g) = v4u{word[0], word[1], word[2], word[3]};
+      __builtin_nontemporal_store(v4u{word[0], word[1], word[2], word[3]}, (v4u *)(codes + vo * 64 + 16 * g));
       if (g == 0) {
         scales[vo] = rng * step_mul;
         zeros[vo] = (uint8_t)z;
       }
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) raw[s] = nxt[s];
+    for (int s = 0; s < 4; ++s) {
+      raw[s] = nxt[s];
+      nxt[s] = nxt2[s];
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_kv_quant(const void *kv, int64_t T, int64_t H, int64_t ld_kv, const int8_t *signs,
-                           uint8_t *codes, float *scales, uint8_t *zeros, hipStream_t stream) {
+namespace {
+template <bool SIGNS>
+hipError_t launch_kv(const void *kv, int64_t T, int64_t H, int64_t ld_kv, const int8_t *signs, uint8_t *codes,
+                     float *scales, uint8_t *zeros, hipStream_t stream) {
   int dev = 0;
   (void)hipGetDevice(&dev);
   int cus = 256;
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   // persistent grid: as many blocks as are resident at once, each wave
-  // walking its tiles with the next one always in flight
+  // walking its tiles with the next two in flight
   static int per_cu = 0;
   if (per_cu == 0) {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kv_quant_kernel, 64 * kWavesPerBlock, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kv_quant_kernel<SIGNS>, 64 * kWavesPerBlock, 0) !=
+            hipSuccess ||
         b < 1)
       b = 1;
     per_cu = b;
@@ -202,9 +231,16 @@ hipError_t launch_kv_quant(const void *kv, int64_t T, int64_t H, int64_t ld_kv, 
   const int64_t cap = (int64_t)cus * per_cu;
   const int64_t grid = blocks < cap ? blocks : cap;
   const float step_mul = (float)(1.0 / (15.0 * __builtin_sqrt(128.0)));
-  kv_quant_kernel<<<dim3((unsigned)grid), dim3(64 * kWavesPerBlock), 0, stream>>>(
+  kv_quant_kernel<SIGNS><<<dim3((unsigned)grid), dim3(64 * kWavesPerBlock), 0, stream>>>(
       (const unsigned short *)kv, T, (int)H, ld_kv, signs, codes, scales, zeros, step_mul);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_kv_quant(const void *kv, int64_t T, int64_t H, int64_t ld_kv, const int8_t *signs,
+                           uint8_t *codes, float *scales, uint8_t *zeros, hipStream_t stream) {
+  return signs != nullptr ? launch_kv<true>(kv, T, H, ld_kv, signs, codes, scales, zeros, stream)
+                          : launch_kv<false>(kv, T, H, ld_kv, signs, codes, scales, zeros, stream);
 }
 
 }  // namespace qr
