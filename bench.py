@@ -280,6 +280,7 @@ def suite(args):
     rq_case("rq_c4_g128", "c4", 16384, 128)
     rq_case("rq_c5", "c5", 64, 0)
     rq_case("rq_c3_kron", "c3", 16384, 0, reps=5)
+    rq_case("rq_d70_kron", "d70", 16384, 0, reps=3)
     gemm_case("gemm_c2", 2048, 12288, 4096, 0)
     gemm_case("gemm_c3", 131072, 4096, 11008, 0, reps=3)
     gemm_case("gemm_c4_g128", 16384, 28672, 8192, 128, reps=3)

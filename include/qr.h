@@ -62,8 +62,9 @@ typedef enum {
  * power of two, e.g. n = 11008 = 64 * 172.  In the Kronecker product the
  * dense index is the fastest: element k = i * dense_m + a.
  *
- * Fields: n = had_n * dense_m, n even, 2 <= n <= 16384, had_n a power of two
- * in [1, 16384], dense_m in [1, 256].  `dense` (device, fp32, row-major
+ * Fields: n = had_n * dense_m, n even, 2 <= n <= 32768, had_n a power of two
+ * in [1, 32768], dense_m in [1, 256], and dense_m <= 16 when n > 16384 (for
+ * example n = 28672 = 4096 * 7).  `dense` (device, fp32, row-major
  * [dense_m][dense_m]) must be NULL iff dense_m == 1; the library does not
  * check that it is orthogonal.  `signs` (device, int8 [n], each +1 or -1,
  * 4-byte aligned) may be NULL for D = I.

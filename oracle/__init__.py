@@ -51,7 +51,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "sylvester_hadamard", "hadamard_entry", "fwht", "rotation_matrix", "rotate",
+    "sylvester_hadamard", "hadamard_entry", "fwht", "rotation_matrix", "rotate", "rotate_kron",
     "quantize_symmetric", "pack_int4", "unpack_int4", "unpack_uint4",
     "rotate_weights", "quantize_weights", "int_gemm", "dequantize_output",
     "dequantize_symmetric", "linear_w4a4", "kv_quantize", "kv_dequantize",
@@ -142,6 +142,27 @@ def rotation_matrix(n: int, had_n: int | None = None, dense=None, signs=None) ->
 def rotate(x, r: np.ndarray) -> np.ndarray:
     """Rotated activations y = x @ R in fp64 (fp16 input converted exactly)."""
     return np.asarray(x).astype(np.float64) @ r
+
+
+def rotate_kron(x, had_n: int, dense, signs=None) -> np.ndarray:
+    """y = x @ rotation_matrix(n, had_n, dense, signs), n = had_n * m, without
+    forming the n x n matrix (for widths where it does not fit in memory).
+
+    With the m-index fastest (k = i*m + a, R3) the Kronecker entry is
+    R[i*m + a, j*m + b] = H[i, j] / sqrt(p) * O[a, b], so x viewed as X[i, a]
+    gives Y = H_p^T X O / sqrt(p) (H_p is symmetric); the signs scale x first
+    (R2).  The tests pin it to the explicit product."""
+    x = np.asarray(x).astype(np.float64)
+    o = np.asarray(dense, dtype=np.float64)
+    m = o.shape[0]
+    n = had_n * m
+    if x.shape[-1] != n:
+        raise ValueError("row width does not match had_n * m")
+    if signs is not None:
+        x = x * np.asarray(signs, dtype=np.float64)
+    z = x.reshape(x.shape[0], had_n, m) @ o          # X[i] O for every i
+    y = fwht(np.swapaxes(z, 1, 2)) / np.sqrt(had_n)  # over i, for every column b
+    return np.swapaxes(y, 1, 2).reshape(x.shape[0], n)
 
 
 # --------------------------------------------------------------------------

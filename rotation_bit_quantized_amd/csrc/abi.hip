@@ -14,10 +14,12 @@ qr_status from_hip(hipError_t e) { return e == hipSuccess ? QR_OK : QR_EDEVICE; 
 qr_status check_rotation(const qr_rotation *rot) {
   if (rot == nullptr) return QR_EINVAL;
   if (rot->n <= 0 || rot->had_n <= 0 || rot->dense_m <= 0) return QR_EINVAL;
-  if (!pow2(rot->had_n) || rot->had_n > 16384) return QR_ESHAPE;
+  if (!pow2(rot->had_n) || rot->had_n > 32768) return QR_ESHAPE;
   if (rot->dense_m > 256) return QR_ESHAPE;
   if (rot->n != rot->had_n * rot->dense_m) return QR_ESHAPE;
-  if (rot->n < 2 || rot->n > 16384 || (rot->n & 1)) return QR_ESHAPE;
+  if (rot->n < 2 || rot->n > 32768 || (rot->n & 1)) return QR_ESHAPE;
+  // rows wider than 16384 are transformed in place in LDS: small dense factors only
+  if (rot->n > 16384 && rot->dense_m > 16) return QR_ESHAPE;
   if ((rot->dense == nullptr) != (rot->dense_m == 1)) return QR_EINVAL;
   if (rot->dense != nullptr && !aligned(rot->dense, 4)) return QR_EALIGN;
   return QR_OK;

@@ -8,7 +8,9 @@
 //   4. max |.| per row or per group, s = max / (7 sqrt(p)), codes
 //      rint(v * 7 / max), packed two per byte.
 // This is the reference-shape path of the library: small or unusual widths
-// (n = 2 .. 16384, any power-of-two Hadamard size, dense factors up to 256).
+// (n = 2 .. 32768, any power-of-two Hadamard size, dense factors up to 256;
+// a factor of size m <= 16 is applied in place, one i-group per thread in
+// registers, so that rows up to 32768 fit in LDS as one fp32 copy).
 // The wide power-of-two and the 64 x m Kronecker shapes have MFMA kernels.
 //
 // Method: QuaRot summary (Elamur Research), "Key points" (RTN on the fly,
@@ -21,6 +23,7 @@ namespace qr {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kInPlaceM = 16;   // dense factors up to this size are applied in place
 
 __global__ __launch_bounds__(kBlock) void rq_generic_kernel(
     const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, int n, int had_n, int dense_m,
@@ -28,10 +31,11 @@ __global__ __launch_bounds__(kBlock) void rq_generic_kernel(
     uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
   extern __shared__ float smem[];
   float *buf = smem;
-  float *tmp = smem + n;
+  const bool in_place = dense_m <= kInPlaceM;
+  float *tmp = smem + n;   // (second row copy: large dense factors only)
   const int g = group ? group : n;
   const int ngroups = n / g;
-  float *red = smem + (dense_m > 1 ? 2 * n : n);
+  float *red = smem + (dense_m > 1 && !in_place ? 2 * n : n);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -47,7 +51,26 @@ __global__ __launch_bounds__(kBlock) void rq_generic_kernel(
     __syncthreads();
 
     float *cur = buf;
-    if (dense_m > 1) {
+    if (dense_m > 1 && in_place) {
+      // one i-group (dense_m consecutive values) per thread, in registers
+      for (int i = tid; i < n / dense_m; i += kBlock) {
+        float xi[kInPlaceM], yi[kInPlaceM];
+#pragma unroll
+        for (int a = 0; a < kInPlaceM; ++a) xi[a] = a < dense_m ? buf[i * dense_m + a] : 0.f;
+#pragma unroll
+        for (int b = 0; b < kInPlaceM; ++b) {
+          float acc = 0.f;
+#pragma unroll
+          for (int a = 0; a < kInPlaceM; ++a)
+            if (a < dense_m && b < dense_m) acc = __builtin_fmaf(xi[a], dense[a * dense_m + b], acc);
+          yi[b] = acc;
+        }
+#pragma unroll
+        for (int b = 0; b < kInPlaceM; ++b)
+          if (b < dense_m) buf[i * dense_m + b] = yi[b];
+      }
+      __syncthreads();
+    } else if (dense_m > 1) {
       for (int idx = tid; idx < n; idx += kBlock) {
         const int i = idx / dense_m;
         const int b = idx - i * dense_m;
@@ -107,7 +130,8 @@ __global__ __launch_bounds__(kBlock) void rq_generic_kernel(
 hipError_t launch_rq_generic(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
                              uint8_t *codes, float *scales, hipStream_t stream) {
   const int g = group ? group : r.n;
-  const size_t lds = sizeof(float) * ((r.dense_m > 1 ? 2 * (size_t)r.n : (size_t)r.n) + (size_t)(r.n / g));
+  const bool two_copies = r.dense_m > kInPlaceM;
+  const size_t lds = sizeof(float) * ((two_copies ? 2 * (size_t)r.n : (size_t)r.n) + (size_t)(r.n / g));
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void *)rq_generic_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -64,7 +64,8 @@ MIS = 0x10001
     (dict(codes=MIS), qr.QR_EALIGN),
     (dict(r=rot(n=4096, had=2048)), qr.QR_ESHAPE),
     (dict(r=rot(n=12, had=12)), qr.QR_ESHAPE),
-    (dict(r=rot(n=16384 * 2, had=8192, m=4, dense=A16)), qr.QR_ESHAPE),
+    (dict(r=rot(n=65536, had=65536)), qr.QR_ESHAPE),                    # wider than 32768
+    (dict(r=rot(n=32768, had=1024, m=32, dense=A16)), qr.QR_ESHAPE),     # > 16384 needs dense_m <= 16
     (dict(r=rot(n=64 * 172, had=64, m=172, dense=None)), qr.QR_EINVAL),
     (dict(r=rot(n=4096, had=4096, m=1, dense=A16)), qr.QR_EINVAL),
     (dict(r=rot(n=3, had=1, m=3, dense=A16)), qr.QR_ESHAPE),

@@ -51,8 +51,14 @@ def gpu_rq(qr, x, n, had_n=None, dense=None, signs=None, group=0, ld=None):
 
 def oracle_rq(x, n, had_n=None, dense=None, signs=None, group=0):
     had_n = n if had_n is None else had_n
-    r = O.rotation_matrix(n, had_n, dense=None if dense is None else np.asarray(dense, np.float64), signs=signs)
-    y = O.rotate(x, r)
+    if dense is not None and n > 12000:   # the explicit n x n matrix would not fit
+        y = O.rotate_kron(x, had_n, np.asarray(dense, np.float64), signs)
+    elif dense is None and n > 16384:
+        d = np.ones(n) if signs is None else np.asarray(signs, np.float64)
+        y = O.fwht(np.asarray(x).astype(np.float64) * d) / np.sqrt(n)
+    else:
+        r = O.rotation_matrix(n, had_n, dense=None if dense is None else np.asarray(dense, np.float64), signs=signs)
+        y = O.rotate(x, r)
     return O.quantize_symmetric(y, group)
 
 
@@ -88,13 +94,21 @@ def test_rq_c4_group128_rows(qr):
     check_rq(qr, x, c.K, signs=W.make_signs(c), group=128)
 
 
+def test_rq_d70_kron_rows(qr):
+    """28672 = 4096 * 7 (LLaMA-2-70B down_proj input): first and last rows."""
+    c = W.CONFIGS["d70"]
+    rows = np.r_[np.arange(96), np.arange(c.M - 33, c.M)]
+    x = W.make_x(c, rows=rows)
+    check_rq(qr, x, c.K, had_n=c.had_n, dense=W.make_dense(c))
+
+
 def test_rq_c3_kron_rows(qr):
     c = W.CONFIGS["c3"]
     x = W.make_x(c, rows=np.arange(257))
     check_rq(qr, x, c.K, had_n=64, dense=W.make_dense(c))
 
 
-@pytest.mark.parametrize("n", [2, 8, 64, 256, 1024, 2048, 4096, 8192, 16384])
+@pytest.mark.parametrize("n", [2, 8, 64, 256, 1024, 2048, 4096, 8192, 16384, 32768])
 @pytest.mark.parametrize("rows", [1, 3, 130])
 def test_rq_widths_and_ragged_rows(qr, n, rows):
     x = W.make_random_rows(rows, n, seed=n * 7 + rows, scale=3.0)

@@ -58,6 +58,21 @@ def test_fwht_equals_explicit_product(n):
 
 # ---------------------------------------------------------------- rotations
 
+@pytest.mark.parametrize("p,m,use_signs", [(4, 3, False), (16, 12, True), (64, 7, True), (8, 172, False),
+                                           (2, 5, True)])
+def test_rotate_kron_equals_explicit_product(p, m, use_signs):
+    """The factored Kronecker rotation (used where the n x n matrix does not
+    fit) is the explicit product x @ R: pinned against np.kron built R."""
+    rng = np.random.default_rng(p * 1000 + m)
+    n = p * m
+    o = np.linalg.qr(rng.standard_normal((m, m)))[0]
+    signs = np.where(rng.random(n) < 0.5, -1, 1).astype(np.int8) if use_signs else None
+    x = rng.standard_normal((5, n)).astype(np.float16)
+    ref = O.rotate(x, O.rotation_matrix(n, p, dense=o, signs=signs))
+    got = O.rotate_kron(x, p, o, signs)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
 @pytest.mark.parametrize("n", [4, 512, 4096])
 def test_rotation_orthogonal(n):
     r = O.rotation_matrix(n, signs=W.make_signs("c2", n))

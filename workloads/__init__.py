@@ -66,6 +66,10 @@ CONFIGS: dict[str, Config] = {
     "c5": Config("c5", 5, "decode step at batch 64: 64x4096 -> 4096, plus KV rows 64x32x128",
                  64, 4096, 4096, 4096, 1, 0, True, "normal", 8, 100.0, 0.0, 0.02,
                  kv=dict(T=64, H=32, D=128, outlier_dims=2, outlier_scale=30.0)),
+    # the second non-power-of-two width: LLaMA-2-70B down_proj input,
+    # 28672 = 4096 * 7, drawn like c3's down_proj input
+    "d70": Config("d70", 6, "LLaMA-2-70B down_proj at 16384 tokens: 16384x28672 -> 8192",
+                  16384, 28672, 8192, 4096, 7, 0, False, "laplace", 0, 200.0, 0.001, 0.01),
 }
 
 
