@@ -72,6 +72,8 @@ qr_status qr_rotate_quant(const void *x_f16, int64_t rows, int64_t ld_x, const q
     return from_hip(qr::launch_rq_pow2(x_f16, rows, ld_x, r, (int)group, codes, scales, s));
   if (qr::rq_kron_supported(r, (int)group))
     return from_hip(qr::launch_rq_kron(x_f16, rows, ld_x, r, (int)group, codes, scales, s));
+  if (qr::rq_kron4096_supported(r, (int)group))
+    return from_hip(qr::launch_rq_kron4096(x_f16, rows, ld_x, r, codes, scales, s));
   return from_hip(qr::launch_rq_generic(x_f16, rows, ld_x, r, (int)group, codes, scales, s));
 }
 

@@ -65,4 +65,76 @@ __device__ __forceinline__ float wave_min(float v) {
   return v;
 }
 
+
+// ---- synchronisation, lane exchange and LDS-DMA helpers
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0), vmcnt and expcnt left alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// 2 x 2 transposes of (register, lane bit 4) and (register, lane bit 5).
+__device__ __forceinline__ void swap16(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane16_swap(f2u(a), f2u(b), false, false);
+  a = u2f(r[0]);
+  b = u2f(r[1]);
+}
+__device__ __forceinline__ void swap32(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane32_swap(f2u(a), f2u(b), false, false);
+  a = u2f(r[0]);
+  b = u2f(r[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return u2f(dpp<CTRL>(f2u(v)));
+}
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Max over the 64 lanes without LDS: DPP within rows of 16, then the
+// row-pair swaps.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));   // lanes i and 7 - i of each half row
+  v = fmaxf(v, dpp<kRowMirror>(v));       // lanes i and 15 - i of each row
+  auto a = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  v = fmaxf(u2f(a[0]), u2f(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  return fmaxf(u2f(b[0]), u2f(b[1]));
+}
+
+// LDS address (byte offset in the workgroup's LDS) of a __shared__ pointer.
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// One wave-instruction of global -> LDS DMA: lane l's 16 bytes at src land at
+// LDS byte dst + 16 l (dst wave-uniform).  Issued from inline assembly: the
+// compiler then does not see an LDS write it would wait for before every
+// later LDS read it cannot prove disjoint (a full memory round trip); the
+// caller orders uses with explicit vmcnt waits.  No register is written (the
+// scratch SGPR keeps m0, which is reserved to the compiler).
+__device__ __forceinline__ void dma16_to_lds(const void *src, unsigned dst) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(dst))
+      : "memory");
+}
+
 }  // namespace qr

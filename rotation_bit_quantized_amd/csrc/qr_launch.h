@@ -32,6 +32,12 @@ bool rq_kron_supported(const RotArgs &r, int group);
 hipError_t launch_rq_kron(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
                           uint8_t *codes, float *scales, hipStream_t stream);
 
+// Rotate + quantize for n = 4096 * m with a dense m x m factor (2 <= m <= 8),
+// H_8 kron O on fp16 MFMA (hi/lo split), 512-point Hadamard in registers.
+bool rq_kron4096_supported(const RotArgs &r, int group);
+hipError_t launch_rq_kron4096(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, uint8_t *codes,
+                              float *scales, hipStream_t stream);
+
 // Integer GEMM.  out_i32 == false: fp16 output with ld_y; true: int32 sums.
 hipError_t launch_gemm_prefill(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,
                                int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,

@@ -48,7 +48,6 @@
 namespace qr {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -67,50 +66,6 @@ constexpr int kCodeOff = 0;                          // codes of one row, four g
 constexpr int kSinkOff = kCodeOff + 4 * kGroupPitch;   // masked-off code writes land here
 constexpr int kMaxOff = kSinkOff + 4 * kGroupPitch;    // the four waves' maxima
 constexpr int kAux = kMaxOff + 16;
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-__device__ __forceinline__ void swap16(float &a, float &b) {
-  auto r = __builtin_amdgcn_permlane16_swap(f2u(a), f2u(b), false, false);
-  a = u2f(r[0]);
-  b = u2f(r[1]);
-}
-__device__ __forceinline__ void swap32(float &a, float &b) {
-  auto r = __builtin_amdgcn_permlane32_swap(f2u(a), f2u(b), false, false);
-  a = u2f(r[0]);
-  b = u2f(r[1]);
-}
-
-template <int CTRL>
-__device__ __forceinline__ unsigned dpp(unsigned v) {
-  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return u2f(dpp<CTRL>(f2u(v)));
-}
-constexpr int kQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
-constexpr int kQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
-
-// Max over the 64 lanes without LDS: DPP within rows of 16, then the
-// row-pair swaps.
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = fmaxf(v, dpp<kQuadXor1>(v));
-  v = fmaxf(v, dpp<kQuadXor2>(v));
-  v = fmaxf(v, dpp<kRowHalfMirror>(v));   // lanes i and 7 - i of each half row
-  v = fmaxf(v, dpp<kRowMirror>(v));       // lanes i and 15 - i of each row
-  auto a = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
-  v = fmaxf(u2f(a[0]), u2f(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
-  return fmaxf(u2f(b[0]), u2f(b[1]));
-}
 
 __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
     const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, int m, const float *__restrict__ dense,
@@ -222,20 +177,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void rq_kron_kernel(
     const int off = 1024 * chunk + 16 * lane;
     dma_src[q] = off < rowb - 16 ? off : rowb - 16;
   }
-  // Issued from inline assembly: the compiler then does not see an LDS
-  // write it would wait for (it cannot tell the A-fragment reads of other
-  // buffers apart and would wait for the whole DMA before each); the
-  // explicit vmcnt waits below order every use.  The DMA writes no
-  // register (the scratch SGPR holds m0 across it).
-  const unsigned smem_lds = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)smem;
+  const unsigned smem_lds = lds_addr(smem);
   auto issue_dma = [&](const uint8_t *src, int bsel, int q) __attribute__((always_inline)) {
-    const unsigned dst = __builtin_amdgcn_readfirstlane(smem_lds + (unsigned)(bsel * kRowBuf + dma_dst[q]));
-    unsigned saved;   // m0 is reserved to the compiler: restore it
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(src + dma_src[q]), "s"(dst)
-        : "memory");
+    dma16_to_lds(src + dma_src[q], smem_lds + (unsigned)(bsel * kRowBuf + dma_dst[q]));
   };
 
   v4f S[2][kMT][kNTW];   // two rows: one in the MFMA phase, one being finished

@@ -51,7 +51,7 @@ def gpu_rq(qr, x, n, had_n=None, dense=None, signs=None, group=0, ld=None):
 
 def oracle_rq(x, n, had_n=None, dense=None, signs=None, group=0):
     had_n = n if had_n is None else had_n
-    if dense is not None and n > 12000:   # the explicit n x n matrix would not fit
+    if dense is not None and n > 4096:   # the explicit n x n matrix grows large
         y = O.rotate_kron(x, had_n, np.asarray(dense, np.float64), signs)
     elif dense is None and n > 16384:
         d = np.ones(n) if signs is None else np.asarray(signs, np.float64)
@@ -175,6 +175,23 @@ def test_rq_kron_fast_path(qr, m, rows):
     x[:, 3] *= 50
     check_rq(qr, x, 64 * m, 64, dense=o)
     check_rq(qr, x, 64 * m, 64, dense=o, ld=64 * m + 24)
+
+
+@pytest.mark.parametrize("m,rows", [(2, 3), (3, 37), (4, 1), (5, 130), (6, 64), (7, 5), (7, 1100), (8, 40)])
+def test_rq_kron4096_fast_path(qr, m, rows):
+    """4096 x m Kronecker rotations without signs (H_8 kron O on MFMA, 512-point
+    transform in registers); 1100 rows give each persistent block several rows.
+    Row 1 is all zero (scale 0, codes 0), row 2 one-hot."""
+    o = np.linalg.qr(np.random.default_rng(40 + m).standard_normal((m, m)))[0].astype(np.float32)
+    x = W.make_random_rows(rows, 4096 * m, seed=m * rows, scale=2.0)
+    x[:, 3] *= 50
+    if rows > 2:
+        x[1] = 0
+        x[2] = 0
+        x[2, 4096 * m - 5] = 3.0
+    check_rq(qr, x, 4096 * m, 4096, dense=o)
+    if rows <= 64:
+        check_rq(qr, x, 4096 * m, 4096, dense=o, ld=4096 * m + 40)
 
 
 def test_rq_zero_rows_noop(qr):
