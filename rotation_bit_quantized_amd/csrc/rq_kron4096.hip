@@ -165,17 +165,34 @@ __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron4096_kernel(
     // every wave has read its A-fragments: the buffer takes the next row
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
-    issue_row(row + stride < rows ? row + stride : row);
+    const uint8_t *nsrc = (const uint8_t *)(x + (row + stride < rows ? row + stride : row) * ld_x);
 
     // ---- 512-point Walsh-Hadamard over t.  Element r of c[mt] is block
     // t = 16 mt + 4 g + r: t0, t1 = r bits, t2, t3 = lane bits 4, 5,
-    // t4..t8 = mt bits.
+    // t4..t8 = mt bits.  First the four bits inside each tile, with the next
+    // row's DMA spread over them (a burst of DMA instructions would stall
+    // the wave on the full memory-instruction queue), then the tile bits.
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
-      v4f &v = c[mt];
-      float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
-      v = v4f{a0 + a2, a1 + a3, a0 - a2, a1 - a3};   // r bits now hold u0 (bit 0), u1 (bit 1)
+      float e0 = c[mt][0], e1 = c[mt][1], e2 = c[mt][2], e3 = c[mt][3];
+      // t0, t1: register bits 0, 1 -> u0, u1
+      float a0 = e0 + e1, a1 = e0 - e1, a2 = e2 + e3, a3 = e2 - e3;
+      e0 = a0 + a2; e1 = a1 + a3; e2 = a0 - a2; e3 = a1 - a3;
+      // t2: lane bit 4 <-> register bit 0 (holding u0), then butterfly over
+      // register bit 0; t3 likewise with lane bit 5 and register bit 1
+      swap16(e0, e1);
+      swap16(e2, e3);
+      float f0 = e0 + e1, f1 = e0 - e1, f2 = e2 + e3, f3 = e2 - e3;
+      swap32(f0, f2);
+      swap32(f1, f3);
+      c[mt] = v4f{f0 + f2, f1 + f3, f0 - f2, f1 - f3};
+      if ((mt & 1) && (mt >> 1) < kDmaPerWave) {
+        const int chunk = (mt >> 1) * kWaves + wave;
+        dma16_to_lds(nsrc + 1024 * chunk + 16 * lane, xrow_lds + 1024 * chunk);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    static_assert(kDmaPerWave <= kMT / 2, "DMA slots in the tile loop");
 #pragma unroll
     for (int mb = 1; mb < kMT; mb <<= 1)
 #pragma unroll
@@ -185,18 +202,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron4096_kernel(
         c[mt] = u + w;
         c[mt | mb] = u - w;
       }
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-      // t2: lane bit 4 <-> register bit 0 (holding u0), then butterfly over
-      // register bit 0; t3 likewise with lane bit 5 and register bit 1
-      float e0 = c[mt][0], e1 = c[mt][1], e2 = c[mt][2], e3 = c[mt][3];
-      swap16(e0, e1);
-      swap16(e2, e3);
-      float f0 = e0 + e1, f1 = e0 - e1, f2 = e2 + e3, f3 = e2 - e3;
-      swap32(f0, f2);
-      swap32(f1, f3);
-      c[mt] = v4f{f0 + f2, f1 + f3, f0 - f2, f1 - f3};
-    }
     // Element r of c[mt] is now Y[u][16 wave + c16] with
     //   u = g | (r & 1) << 2 | (r >> 1) << 3 | mt << 4
     // (columns n >= 8 M hold zero: B's padding is zero).
