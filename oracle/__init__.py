@@ -45,6 +45,11 @@ Readings where the pages are silent (each repeated where it is used):
      step = 0, z = 0, q = 0.
   R13 Output dequantization in fp64: y = acc * s_x * s_w, or for groups the sum
      over groups of acc_g * s_x[g] * s_w[g].
+  R14 Decode attention over the 4-bit KV cache: the query stays in full
+     precision, keys and values are the dequantized cache rotated back to the
+     original basis, softmax is unquantized; out = softmax(c q K^T) V over the
+     first len tokens of the sequence, query head h reading KV head
+     h // (Hq / Hkv); an empty sequence gives zeros.
 """
 from __future__ import annotations
 
@@ -55,6 +60,7 @@ __all__ = [
     "quantize_symmetric", "pack_int4", "unpack_int4", "unpack_uint4",
     "rotate_weights", "quantize_weights", "int_gemm", "dequantize_output",
     "dequantize_symmetric", "linear_w4a4", "kv_quantize", "kv_dequantize",
+    "kv_attention_decode",
 ]
 
 
@@ -335,3 +341,49 @@ def kv_quantize(kv, signs=None):
 def kv_dequantize(q, step, z) -> np.ndarray:
     """(q - z) * step, the rotated-domain reconstruction."""
     return (np.asarray(q, np.float64) - np.asarray(z, np.float64)[..., None]) * np.asarray(step, np.float64)[..., None]
+
+
+# --------------------------------------------------------------------------
+# Decode attention over the 4-bit KV cache
+# --------------------------------------------------------------------------
+
+def kv_attention_decode(q, k_codes, k_step, k_zero, v_codes, v_step, v_zero, lens=None, signs=None,
+                        sm_scale=None):
+    """One decode step of attention reading the rotated 4-bit KV cache (R14).
+
+    [QuaRot-abs]: computational invariance applied to the attention mechanism
+    and the KV cache, the cache held in 4 bits.  [DuQuant] Knowl 12: the
+    Query x Key and attention-output x Value products pass through fixed
+    head-wise Hadamard rotations, with the softmax output left unquantized.
+
+    q       fp16/fp64 [B, Hq, D]
+    k_codes uint8 [B, T, Hkv, D] unsigned codes (unpacked), k_step fp [B, T, Hkv],
+            k_zero int [B, T, Hkv]; likewise v_*.
+    lens    int [B] tokens per sequence (default all T).
+    signs   the +-1 vector the cache was rotated with (R12), or None.
+    Returns fp64 [B, Hq, D].
+
+    Keys and values are reconstructed in the original basis:
+    K = ((q - z) * step) @ R^T with R = diag(signs) H_D / sqrt(D)."""
+    qf = np.asarray(q, np.float64)
+    b_, hq, d = qf.shape
+    t_, hkv = np.asarray(k_codes).shape[1:3]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    lens = np.full(b_, t_, dtype=np.int64) if lens is None else np.asarray(lens, np.int64)
+    r = rotation_matrix(d, d, signs=signs)
+    k = kv_dequantize(k_codes, k_step, k_zero) @ r.T     # [B, T, Hkv, D]
+    v = kv_dequantize(v_codes, v_step, v_zero) @ r.T
+    group = hq // hkv
+    out = np.zeros((b_, hq, d))
+    for b in range(b_):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        for h in range(hq):
+            kh = k[b, :n, h // group, :]                   # [n, D]
+            vh = v[b, :n, h // group, :]
+            s = sm_scale * (kh @ qf[b, h])                  # [n]
+            e = np.exp(s - s.max())
+            out[b, h] = (e / e.sum()) @ vh
+    return out

@@ -447,3 +447,100 @@ def test_generators_are_seeded_and_row_subsets_consistent():
     assert cols.size == 8
     assert np.abs(b[:, cols].astype(np.float64)).mean() > 50 * np.abs(b.astype(np.float64)).mean(axis=0).min()
     assert np.array_equal(W.make_signs(c), W.make_signs(c))
+
+
+# ------------------------------------------------------------ decode attention
+
+def _attn_inputs(b, t, hq, hkv, d, seed):
+    rng = np.random.default_rng(seed)
+    kc = rng.integers(0, 16, size=(b, t, hkv, d)).astype(np.uint8)
+    vc = rng.integers(0, 16, size=(b, t, hkv, d)).astype(np.uint8)
+    ks = rng.uniform(0.02, 0.3, size=(b, t, hkv))
+    vs = rng.uniform(0.02, 0.3, size=(b, t, hkv))
+    kz = rng.integers(0, 16, size=(b, t, hkv))
+    vz = rng.integers(0, 16, size=(b, t, hkv))
+    q = rng.standard_normal((b, hq, d)).astype(np.float16)
+    return q, kc, ks, kz, vc, vs, vz
+
+
+def test_attn_worked_example():
+    """D = 2, R = H_2 / sqrt(2), unit steps, zero points 0, sm_scale 1.
+    Rotated keys (0, 0) and (1, 1) reconstruct to K0 = 0, K1 = (sqrt2, 0);
+    q = (ln 3 / sqrt2, 0) scores them 0 and ln 3, so p = (1/4, 3/4).  Rotated
+    values (2, 0) and (0, 2) reconstruct to (sqrt2, sqrt2) and (sqrt2, -sqrt2):
+    out = (sqrt2, -sqrt2 / 2)."""
+    one = np.ones((1, 2, 1))
+    zero = np.zeros((1, 2, 1), np.int64)
+    kc = np.array([[[[0, 0]], [[1, 1]]]], np.uint8)
+    vc = np.array([[[[2, 0]], [[0, 2]]]], np.uint8)
+    q = np.array([[[np.log(3) / np.sqrt(2), 0.0]]])
+    out = O.kv_attention_decode(q, kc, one, zero, vc, one, zero, sm_scale=1.0)
+    assert out[0, 0] == pytest.approx([np.sqrt(2), -np.sqrt(2) / 2], abs=1e-14)
+
+
+def test_attn_brute_force_tiny():
+    """Pure-Python loops from the definition: unpack, dequantize, undo the
+    rotation entry by entry (signs and popcount Hadamard), score, softmax with
+    math.exp, weighted sum; ragged lengths and grouped query heads."""
+    import math
+    b_, t_, hq, hkv, d = 2, 3, 4, 2, 8
+    q, kc, ks, kz, vc, vs, vz = _attn_inputs(b_, t_, hq, hkv, d, 5)
+    signs = [1, -1, -1, 1, 1, 1, -1, 1]
+    lens = [3, 2]
+    sm = 0.7
+
+    def orig(codes, step, zero, b, t, h):
+        rot = [(int(codes[b, t, h, j]) - int(zero[b, t, h])) * float(step[b, t, h]) for j in range(d)]
+        # rotated = v R with R[i][j] = signs[i] H[i][j] / sqrt(d); v = rotated R^T
+        return [sum(rot[j] * signs[i] * (-1) ** bin(i & j).count("1") for j in range(d)) / math.sqrt(d)
+                for i in range(d)]
+
+    got = O.kv_attention_decode(q, kc, ks, kz, vc, vs, vz, lens=lens, signs=np.array(signs), sm_scale=sm)
+    for b in range(b_):
+        for h in range(hq):
+            g = h // (hq // hkv)
+            sc = [sm * sum(float(q[b, h, i]) * k for i, k in enumerate(orig(kc, ks, kz, b, t, g)))
+                  for t in range(lens[b])]
+            mx = max(sc)
+            e = [math.exp(s - mx) for s in sc]
+            want = [sum(e[t] * orig(vc, vs, vz, b, t, g)[i] for t in range(lens[b])) / sum(e) for i in range(d)]
+            assert got[b, h] == pytest.approx(want, rel=1e-12, abs=1e-12)
+
+
+def test_attn_single_token_and_uniform_cases():
+    q, kc, ks, kz, vc, vs, vz = _attn_inputs(2, 5, 4, 4, 128, 6)
+    r = O.rotation_matrix(128)
+    vrec = O.kv_dequantize(vc, vs, vz) @ r.T
+    # one token: softmax of a single score is 1 -> out = that token's value
+    out = O.kv_attention_decode(q, kc, ks, kz, vc, vs, vz, lens=[1, 1])
+    assert np.allclose(out, vrec[:, 0], rtol=0, atol=1e-12)
+    # identical keys (or sm_scale 0): uniform weights -> mean of the values
+    kc2 = np.repeat(kc[:, :1], 5, axis=1)
+    ks2 = np.repeat(ks[:, :1], 5, axis=1)
+    kz2 = np.repeat(kz[:, :1], 5, axis=1)
+    out = O.kv_attention_decode(q, kc2, ks2, kz2, vc, vs, vz)
+    assert np.allclose(out, vrec.mean(axis=1), rtol=0, atol=1e-12)
+    out = O.kv_attention_decode(q, kc, ks, kz, vc, vs, vz, sm_scale=0.0)
+    assert np.allclose(out, vrec.mean(axis=1), rtol=0, atol=1e-12)
+    # empty sequence -> zeros
+    out = O.kv_attention_decode(q, kc, ks, kz, vc, vs, vz, lens=[0, 3])
+    assert np.all(out[0] == 0) and np.any(out[1] != 0)
+
+
+def test_attn_rotated_domain_identity():
+    """R is orthogonal, so attention in the rotated basis - query rotated by R,
+    cache used as stored, output rotated back by R^T - equals the oracle's
+    original-basis attention (the identity the GPU kernel uses)."""
+    signs = np.where(np.random.default_rng(3).random(128) < 0.5, -1, 1)
+    q, kc, ks, kz, vc, vs, vz = _attn_inputs(1, 7, 8, 2, 128, 7)
+    r = O.rotation_matrix(128, signs=signs)
+    krot = O.kv_dequantize(kc, ks, kz)
+    vrot = O.kv_dequantize(vc, vs, vz)
+    qr_ = q.astype(np.float64) @ r
+    want = np.zeros((1, 8, 128))
+    for h in range(8):
+        s = krot[0, :, h // 4] @ qr_[0, h] / np.sqrt(128)
+        p = np.exp(s - s.max())
+        want[0, h] = (p / p.sum()) @ vrot[0, :, h // 4] @ r.T
+    got = O.kv_attention_decode(q, kc, ks, kz, vc, vs, vz, signs=signs)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
