@@ -159,6 +159,52 @@ qr_status qr_kv_quant(const void *kv_f16, int64_t T, int64_t H, int64_t head_dim
                       uint8_t *codes, float *scales, uint8_t *zeros, void *stream);
 
 /*
+ * One decode step of attention over the rotated 4-bit KV cache (QuaRot
+ * abstract: computational invariance of the attention mechanism and the KV
+ * cache under the rotation, the cache held in 4 bits; DuQuant page, Knowl 12:
+ * Query x Key and attention output x Value pass through fixed head-wise
+ * Hadamard rotations, the softmax output stays unquantized).
+ *
+ * For sequence b and query head h (KV head g = h / (Hq / Hkv)), over the
+ * tokens t < lens[b] of the cache written by qr_kv_quant with the same signs:
+ *   K_t = ((c_t - z_t) step_t) R^T,   V_t likewise,   R = diag(signs) H_128 / sqrt(128)
+ *   out = sum_t softmax_t(sm_scale q . K_t) V_t            (fp32 inside)
+ * computed as ((q R) against the stored rotated cache) R^T.  An empty
+ * sequence (lens[b] == 0 or T == 0) gives zeros.
+ *
+ * q_f16     device fp16 [B][Hq][128] (2-byte aligned)
+ * k_codes   device [B][T][Hkv][64] packed unsigned codes, as qr_kv_quant
+ *           writes them for B*T tokens (16-byte aligned); v_codes likewise.
+ * k_scales  device fp32 [B][T][Hkv] steps; k_zeros device uint8 [B][T][Hkv]
+ *           zero points; v_* likewise.
+ * lens      device int32 [B], tokens per sequence (clamped to [0, T]), or NULL
+ *           for T everywhere.
+ * signs     device int8 [128] of +-1 the cache was quantized with, or NULL.
+ * sm_scale  softmax scale, typically 1/sqrt(128); finite.
+ * workspace device scratch of at least qr_kv_attn_decode_workspace(...) bytes
+ *           (16-byte aligned) when that size is non-zero: a sequence is then
+ *           split into chunks of tokens whose partial results are merged by a
+ *           second kernel.  NULL with workspace_bytes == 0 runs one chunk per
+ *           sequence instead (no workspace; fewer blocks for small batches).
+ *           A non-NULL workspace smaller than required gives QR_EINVAL.
+ * out_f16   device fp16 [B][Hq][128] (2-byte aligned).
+ * Hq % Hkv == 0; head_dim == 128.  The caller owns every buffer; concurrent
+ * calls must not share a workspace.
+ */
+qr_status qr_kv_attn_decode(const void *q_f16, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                            int64_t head_dim, const uint8_t *k_codes, const float *k_scales,
+                            const uint8_t *k_zeros, const uint8_t *v_codes, const float *v_scales,
+                            const uint8_t *v_zeros, const int32_t *lens, const int8_t *signs,
+                            float sm_scale, void *workspace, int64_t workspace_bytes, void *out_f16,
+                            void *stream);
+
+/*
+ * Workspace bytes qr_kv_attn_decode needs for this shape (0: none).  Depends
+ * on B, Hq and T only.  Host-only; launches nothing.
+ */
+qr_status qr_kv_attn_decode_workspace(int64_t B, int64_t Hq, int64_t T, int64_t head_dim, int64_t *bytes);
+
+/*
  * Test and diagnostic export: the exact integer sums of qr_int4_gemm without
  * the epilogue, from the same kernels.  acc is int32 [M][N] (group 0) or
  * [K/group][M][N] (one slice per group), contiguous.  Same argument rules as

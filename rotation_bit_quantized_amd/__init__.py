@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "QRError", "LibraryNotBuilt", "Rotation", "library", "library_path", "rotate_quant", "int4_gemm",
-    "int4_gemm_i32", "kv_quant", "status_str", "version", "EXPORTS",
+    "int4_gemm_i32", "kv_quant", "kv_attn_decode", "kv_attn_decode_workspace", "status_str", "version",
+    "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,8 +30,8 @@ _LIB_PATH = os.path.join(_HERE, "libqr.so")
 _lib = None
 
 QR_OK, QR_EINVAL, QR_ESHAPE, QR_EALIGN, QR_EDEVICE = 0, 1, 2, 3, 4
-EXPORTS = ("qr_rotate_quant", "qr_int4_gemm", "qr_kv_quant", "qr_int4_gemm_i32", "qr_status_str",
-           "qr_version")
+EXPORTS = ("qr_rotate_quant", "qr_int4_gemm", "qr_kv_quant", "qr_int4_gemm_i32", "qr_kv_attn_decode",
+           "qr_kv_attn_decode_workspace", "qr_status_str", "qr_version")
 
 
 class QRError(RuntimeError):
@@ -69,6 +70,11 @@ def library():
     lib.qr_int4_gemm_i32.restype = st
     lib.qr_kv_quant.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.qr_kv_quant.restype = st
+    lib.qr_kv_attn_decode.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      ctypes.c_float, vp, i64, vp, vp]
+    lib.qr_kv_attn_decode.restype = st
+    lib.qr_kv_attn_decode_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
+    lib.qr_kv_attn_decode_workspace.restype = st
     lib.qr_status_str.argtypes = [st]
     lib.qr_status_str.restype = ctypes.c_char_p
     lib.qr_version.argtypes = []
@@ -219,3 +225,60 @@ def kv_quant(kv: torch.Tensor, signs=None, codes=None, scales=None, zeros=None, 
                                _ptr(zeros), _stream(stream))
     _check("qr_kv_quant", st)
     return codes, scales, zeros
+
+
+def kv_attn_decode_workspace(B: int, Hq: int, T: int, head_dim: int = 128) -> int:
+    """Bytes of workspace qr_kv_attn_decode needs for this shape (host only)."""
+    out = ctypes.c_int64(0)
+    _check("qr_kv_attn_decode_workspace",
+           library().qr_kv_attn_decode_workspace(int(B), int(Hq), int(T), int(head_dim), ctypes.byref(out)))
+    return int(out.value)
+
+
+def kv_attn_decode(q, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros, lens=None, signs=None,
+                   sm_scale=None, out=None, workspace=None, stream=None):
+    """qr_kv_attn_decode: one decode step of attention over the rotated 4-bit
+    KV cache.  q fp16 [B, Hq, 128]; k_codes/v_codes uint8 [B, T, Hkv, 64]
+    (or [B*T, Hkv, 64] with B taken from q); scales fp32 and zeros uint8
+    [B, T, Hkv]; lens int32 [B] or None.  A workspace of the size
+    kv_attn_decode_workspace reports is allocated here when not given
+    (pass workspace=False to run without one).  Returns out fp16 [B, Hq, 128]."""
+    _need(q, torch.float16, "q")
+    for t, dt, name in ((k_codes, torch.uint8, "k_codes"), (v_codes, torch.uint8, "v_codes"),
+                        (k_scales, torch.float32, "k_scales"), (v_scales, torch.float32, "v_scales"),
+                        (k_zeros, torch.uint8, "k_zeros"), (v_zeros, torch.uint8, "v_zeros")):
+        _need(t, dt, name)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
+    B, Hq, D = q.shape
+    if k_codes.dim() == 4:
+        T, Hkv = k_codes.shape[1], k_codes.shape[2]
+    elif k_codes.dim() == 3:
+        T, Hkv = k_codes.shape[0] // max(B, 1), k_codes.shape[1]
+    else:
+        raise ValueError("k_codes must be [B, T, Hkv, 64] or [B*T, Hkv, 64]")
+    dev = q.device
+    if sm_scale is None:
+        sm_scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    ln = None
+    if lens is not None:
+        ln = torch.as_tensor(lens, dtype=torch.int32).to(dev).contiguous()
+    sg = None
+    if signs is not None:
+        sg = torch.as_tensor(signs, dtype=torch.int8).to(dev).contiguous()
+    if workspace is False:
+        ws, ws_bytes = None, 0
+    else:
+        if workspace is None:
+            need = kv_attn_decode_workspace(B, Hq, T, D)
+            workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+        ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
+    st = library().qr_kv_attn_decode(_ptr(q), B, Hq, Hkv, T, D, _ptr(k_codes), _ptr(k_scales), _ptr(k_zeros),
+                                     _ptr(v_codes), _ptr(v_scales), _ptr(v_zeros), _ptr(ln), _ptr(sg),
+                                     float(sm_scale), _ptr(ws), ws_bytes, _ptr(out), _stream(stream))
+    _check("qr_kv_attn_decode", st)
+    return out

@@ -123,4 +123,49 @@ qr_status qr_kv_quant(const void *kv_f16, int64_t T, int64_t H, int64_t head_dim
   return from_hip(qr::launch_kv_quant(kv_f16, T, H, ld_kv, signs, codes, scales, zeros, (hipStream_t)stream));
 }
 
+qr_status qr_kv_attn_decode_workspace(int64_t B, int64_t Hq, int64_t T, int64_t head_dim, int64_t *bytes) {
+  if (bytes == nullptr || B < 0 || Hq < 0 || T < 0) return QR_EINVAL;
+  if (head_dim != 128) return QR_ESHAPE;
+  *bytes = qr::attn_decode_plan(B, Hq, T).workspace_bytes;
+  return QR_OK;
+}
+
+qr_status qr_kv_attn_decode(const void *q_f16, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t head_dim,
+                            const uint8_t *k_codes, const float *k_scales, const uint8_t *k_zeros,
+                            const uint8_t *v_codes, const float *v_scales, const uint8_t *v_zeros,
+                            const int32_t *lens, const int8_t *signs, float sm_scale, void *workspace,
+                            int64_t workspace_bytes, void *out_f16, void *stream) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || T < 0) return QR_EINVAL;
+  if (head_dim != 128) return QR_ESHAPE;
+  if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return QR_ESHAPE;
+  if (B > 65535 || Hq > 65535 || T > ((int64_t)1 << 30) || B * T * Hkv > ((int64_t)1 << 40)) return QR_ESHAPE;
+  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return QR_EINVAL;
+  if (workspace_bytes < 0) return QR_EINVAL;
+  if (B == 0 || Hq == 0) return QR_OK;
+  if (q_f16 == nullptr || out_f16 == nullptr) return QR_EINVAL;
+  if (T > 0 && (k_codes == nullptr || k_scales == nullptr || k_zeros == nullptr || v_codes == nullptr ||
+                v_scales == nullptr || v_zeros == nullptr))
+    return QR_EINVAL;
+  if (!aligned(q_f16, 2) || !aligned(out_f16, 2)) return QR_EALIGN;
+  if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
+    return QR_EALIGN;
+  if ((lens != nullptr && !aligned(lens, 4)) || (signs != nullptr && !aligned(signs, 4))) return QR_EALIGN;
+  qr::AttnPlan plan = qr::attn_decode_plan(B, Hq, T);
+  if (plan.splits > 1) {
+    if (workspace == nullptr && workspace_bytes == 0) {
+      // no workspace: one chunk per sequence
+      plan.chunk = T > 0 ? (T + 63) / 64 * 64 : 64;
+      plan.splits = 1;
+      plan.workspace_bytes = 0;
+    } else if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
+      return QR_EINVAL;
+    } else if (!aligned(workspace, 16)) {
+      return QR_EALIGN;
+    }
+  }
+  return from_hip(qr::launch_attn_decode(q_f16, B, Hq, Hkv, T, k_codes, k_scales, k_zeros, v_codes, v_scales,
+                                         v_zeros, lens, signs, sm_scale, plan, (float *)workspace, out_f16,
+                                         (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -46,6 +46,20 @@ hipError_t launch_gemm_decode(const uint8_t *a, const float *sa, const uint8_t *
                               int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
                               bool out_i32, hipStream_t stream);
 
+// Decode attention over the rotated 4-bit KV cache, head_dim 128.  The plan
+// (tokens per chunk, chunks per sequence, workspace size) depends on the
+// shape only.
+struct AttnPlan {
+  int64_t chunk;
+  int64_t splits;
+  int64_t workspace_bytes;
+};
+AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t T);
+hipError_t launch_attn_decode(const void *q, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, const uint8_t *kc,
+                              const float *ks, const uint8_t *kz, const uint8_t *vc, const float *vs,
+                              const uint8_t *vz, const int *lens, const int8_t *signs, float sm_scale,
+                              const AttnPlan &plan, float *ws, void *out, hipStream_t stream);
+
 // KV-cache quantizer, head_dim 128.
 hipError_t launch_kv_quant(const void *kv, int64_t T, int64_t H, int64_t ld_kv, const int8_t *signs,
                            uint8_t *codes, float *scales, uint8_t *zeros, hipStream_t stream);

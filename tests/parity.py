@@ -10,6 +10,11 @@ CPU oracle under the stated tolerances.
 * fp16 outputs: relative Frobenius error <= OUT_REL_FRO against the oracle's
   fp64 dequantized output from the oracle's codes.
 * Scales: relative error <= SCALE_RTOL (fp32 transform vs fp64).
+* Decode attention outputs (fp16): per (sequence, head) relative Frobenius
+  error <= ATTN_REL_FRO and every element within ATTN_ABS_FRAC of that head's
+  largest |output|.  The output's own fp16 rounding is at most 2^-12 relative;
+  fp32 scores, exponentials and sums over up to 10^5 tokens add well under
+  1e-5; the bound leaves a factor of ~2 over fp16 rounding.
 """
 from __future__ import annotations
 
@@ -21,6 +26,8 @@ BOUNDARY_WINDOW = 1e-3
 MAX_MISMATCH_FRAC = 1e-4
 OUT_REL_FRO = 2e-3
 SCALE_RTOL = 1e-5
+ATTN_REL_FRO = 1e-3
+ATTN_ABS_FRAC = 1e-3
 
 
 def near_half(t: np.ndarray) -> np.ndarray:
@@ -93,3 +100,19 @@ def check_kv(gpu_codes, gpu_step, gpu_zero, kv, signs=None):
         err = np.abs(rec - y)[zmis]
         assert np.all(err <= (np.asarray(gpu_step, np.float64)[zmis][:, None] * (1.0 + 1e-4)))
     return int(mism.sum()), int(zmis.sum())
+
+
+def check_attn(gpu_fp16: np.ndarray, ref: np.ndarray, what: str = "attention"):
+    g = np.asarray(gpu_fp16, np.float64)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.sqrt(((g - ref) ** 2).sum(-1))
+    nrm = np.sqrt((ref ** 2).sum(-1))
+    zero = nrm == 0
+    assert np.all(err[zero] == 0), f"{what}: non-zero output where the oracle gives zeros"
+    rel = err[~zero] / nrm[~zero]
+    assert rel.size == 0 or rel.max() <= ATTN_REL_FRO, f"{what}: worst per-head rel fro {rel.max():.3e}"
+    peak = np.abs(ref).max(-1, keepdims=True)
+    assert np.all(np.abs(g - ref) <= ATTN_ABS_FRAC * peak + 1e-30), \
+        f"{what}: max element error {np.abs(g - ref).max():.3e}"
+    return float(rel.max()) if rel.size else 0.0

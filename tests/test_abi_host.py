@@ -142,3 +142,53 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 4096, dtype=torch.float16)
     with pytest.raises(ValueError):
         qr.rotate_quant(x, object())
+
+
+def _attn(lib, **a):
+    f32 = ctypes.c_float
+    return lib.qr_kv_attn_decode(a.get("q", A16), a.get("B", 1), a.get("Hq", 32), a.get("Hkv", 32),
+                                 a.get("T", 4096), a.get("D", 128), a.get("kc", A16), A16, A16,
+                                 a.get("vc", A16), A16, a.get("vz", A16), a.get("lens", None), None,
+                                 f32(a.get("sm", 0.088)), a.get("ws", None), a.get("wsb", 0),
+                                 a.get("out", A16), None)
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(D=64), qr.QR_ESHAPE),
+    (dict(Hkv=3), qr.QR_ESHAPE),
+    (dict(Hkv=0), qr.QR_ESHAPE),
+    (dict(B=-1), qr.QR_EINVAL),
+    (dict(T=-5), qr.QR_EINVAL),
+    (dict(q=None), qr.QR_EINVAL),
+    (dict(out=None), qr.QR_EINVAL),
+    (dict(vz=None), qr.QR_EINVAL),
+    (dict(kc=MIS), qr.QR_EALIGN),
+    (dict(vc=MIS), qr.QR_EALIGN),
+    (dict(lens=MIS), qr.QR_EALIGN),
+    (dict(sm=float("nan")), qr.QR_EINVAL),
+    (dict(ws=A16, wsb=16), qr.QR_EINVAL),        # a workspace smaller than the split needs
+    (dict(ws=None, wsb=1 << 20), qr.QR_EINVAL),  # a size without a buffer
+    (dict(ws=MIS, wsb=1 << 30), qr.QR_EALIGN),
+    (dict(wsb=-1), qr.QR_EINVAL),
+])
+def test_attn_rejects(args, expect):
+    assert _attn(qr.library(), **args) == expect
+
+
+def test_attn_empty_batch_is_noop():
+    assert _attn(qr.library(), B=0, q=None, out=None, kc=None, vc=None) == qr.QR_OK
+    assert _attn(qr.library(), Hq=0, Hkv=0, q=None, out=None) == qr.QR_OK
+
+
+def test_attn_workspace_size():
+    """One decode query per head over 4096 tokens is split into 16 chunks of
+    256 tokens (32 heads x 16 partials of 132 floats); a 64-sequence batch
+    fills the chip without splitting and needs none."""
+    assert qr.kv_attn_decode_workspace(1, 32, 4096) == 32 * 16 * 132 * 4
+    assert qr.kv_attn_decode_workspace(64, 32, 2048) == 0
+    assert qr.kv_attn_decode_workspace(4, 32, 100) == 0
+    with pytest.raises(qr.QRError):
+        qr.kv_attn_decode_workspace(1, 32, 4096, head_dim=64)
+    out = ctypes.c_int64(0)
+    assert qr.library().qr_kv_attn_decode_workspace(1, 32, -1, 128, ctypes.byref(out)) == qr.QR_EINVAL
+    assert qr.library().qr_kv_attn_decode_workspace(1, 32, 1, 128, None) == qr.QR_EINVAL

@@ -249,3 +249,32 @@ def make_random_scales(n: int, seed: int, lo: float = 0.001, hi: float = 0.05) -
     """Uniform positive float32 scales in [lo, hi)."""
     return (_rng(903, seed).random(n) * (hi - lo) + lo).astype(np.float32)
 
+
+
+def make_attn_cache(B: int, T: int, Hkv: int, seed: int, D: int = 128):
+    """A synthetic 4-bit KV cache as the KV quantizer lays it out, for decode
+    attention: codes uint8 [B, T, Hkv, D/2] (uniform bytes: two uniform 4-bit
+    codes each), steps fp32 [B, T, Hkv] uniform in [0.02, 0.3), zero points
+    uint8 [B, T, Hkv] uniform in [0, 15], for K (stream 0) and V (stream 1),
+    drawn in blocks of 1024 tokens keyed [904, seed, stream, block].
+    Returns (kc, ks, kz, vc, vs, vz)."""
+    out = []
+    for stream in (0, 1):
+        c = np.empty((B, T, Hkv, D // 2), np.uint8)
+        s = np.empty((B, T, Hkv), np.float32)
+        z = np.empty((B, T, Hkv), np.uint8)
+        for b0 in range(0, max(T, 1), 1024):
+            b1 = min(b0 + 1024, T)
+            if b1 <= b0:
+                break
+            r = _rng(904, seed, stream, b0 // 1024)
+            c[:, b0:b1] = r.integers(0, 256, size=(B, b1 - b0, Hkv, D // 2), dtype=np.uint8)
+            s[:, b0:b1] = (r.random((B, b1 - b0, Hkv)) * 0.28 + 0.02).astype(np.float32)
+            z[:, b0:b1] = r.integers(0, 16, size=(B, b1 - b0, Hkv), dtype=np.uint8)
+        out += [c, s, z]
+    return tuple(out)
+
+
+def make_attn_query(B: int, Hq: int, seed: int, D: int = 128) -> np.ndarray:
+    """Decode queries, fp16 [B, Hq, D] N(0, 1) (key [905, seed])."""
+    return _rng(905, seed).standard_normal((B, Hq, D)).astype(np.float16)
