@@ -276,6 +276,26 @@ def suite(args):
              GBs=round(nbytes / ms / 1e6, 1), frac_hbm=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
              bytes=nbytes, buffers=len(ks))
 
+    def attn_case(name, B, T, Hq, Hkv, reps=20):
+        if only and name not in only:
+            return
+        kc = torch.randint(0, 256, (B, T, Hkv, 64), dtype=torch.uint8, device=dev, generator=g)
+        vc = torch.randint(0, 256, (B, T, Hkv, 64), dtype=torch.uint8, device=dev, generator=g)
+        ks = torch.rand((B, T, Hkv), device=dev, generator=g) * 0.28 + 0.02
+        vs = torch.rand((B, T, Hkv), device=dev, generator=g) * 0.28 + 0.02
+        kz = torch.randint(0, 16, (B, T, Hkv), dtype=torch.uint8, device=dev, generator=g)
+        vz = torch.randint(0, 16, (B, T, Hkv), dtype=torch.uint8, device=dev, generator=g)
+        q = torch.randn((B, Hq, 128), device=dev, generator=g).half()
+        out = torch.empty_like(q)
+        wsb = qr.kv_attn_decode_workspace(B, Hq, Hkv, T)
+        ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev)
+        nbytes = B * T * Hkv * (2 * 64 + 2 * 5) + 2 * B * Hq * 128 * 2
+        ms = time_each(lambda i: qr.kv_attn_decode(q, kc, ks, kz, vc, vs, vz, out=out, workspace=ws), reps,
+                       torch.cuda.current_stream())
+        emit(name, kernel="qr_kv_attn_decode", shape=[B, T, Hq, Hkv], us=round(ms * 1e3, 3),
+             GBs=round(nbytes / ms / 1e6, 1), frac_hbm=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+             bytes=nbytes, workspace=wsb)
+
     rq_case("rq_c2", "c2", 2048, 0)
     rq_case("rq_c4_g128", "c4", 16384, 128)
     rq_case("rq_c5", "c5", 64, 0)
@@ -288,6 +308,9 @@ def suite(args):
     gemm_case("gemm_c5_decode_streamed", 64, 4096, 4096, 0, reps=128, stream_w=64)
     kv_case("kv_c5_decode", 64, reps=50, cycle=False)
     kv_case("kv_prefill_131072", 131072, reps=5)
+    attn_case("attn_decode_b64_t2048", 64, 2048, 32, 32)
+    attn_case("attn_decode_b1_t4096", 1, 4096, 32, 32, reps=50)
+    attn_case("attn_decode_gqa_b64_t2048", 64, 2048, 64, 8)
 
 
 def main():

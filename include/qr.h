@@ -200,9 +200,10 @@ qr_status qr_kv_attn_decode(const void *q_f16, int64_t B, int64_t Hq, int64_t Hk
 
 /*
  * Workspace bytes qr_kv_attn_decode needs for this shape (0: none).  Depends
- * on B, Hq and T only.  Host-only; launches nothing.
+ * on the shape only, not on the device.  Host-only; launches nothing.
  */
-qr_status qr_kv_attn_decode_workspace(int64_t B, int64_t Hq, int64_t T, int64_t head_dim, int64_t *bytes);
+qr_status qr_kv_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t head_dim,
+                                      int64_t *bytes);
 
 /*
  * Test and diagnostic export: the exact integer sums of qr_int4_gemm without

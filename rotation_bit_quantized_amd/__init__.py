@@ -73,7 +73,7 @@ def library():
     lib.qr_kv_attn_decode.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_float, vp, i64, vp, vp]
     lib.qr_kv_attn_decode.restype = st
-    lib.qr_kv_attn_decode_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
+    lib.qr_kv_attn_decode_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.qr_kv_attn_decode_workspace.restype = st
     lib.qr_status_str.argtypes = [st]
     lib.qr_status_str.restype = ctypes.c_char_p
@@ -227,11 +227,12 @@ def kv_quant(kv: torch.Tensor, signs=None, codes=None, scales=None, zeros=None, 
     return codes, scales, zeros
 
 
-def kv_attn_decode_workspace(B: int, Hq: int, T: int, head_dim: int = 128) -> int:
+def kv_attn_decode_workspace(B: int, Hq: int, Hkv: int, T: int, head_dim: int = 128) -> int:
     """Bytes of workspace qr_kv_attn_decode needs for this shape (host only)."""
     out = ctypes.c_int64(0)
     _check("qr_kv_attn_decode_workspace",
-           library().qr_kv_attn_decode_workspace(int(B), int(Hq), int(T), int(head_dim), ctypes.byref(out)))
+           library().qr_kv_attn_decode_workspace(int(B), int(Hq), int(Hkv), int(T), int(head_dim),
+                                                 ctypes.byref(out)))
     return int(out.value)
 
 
@@ -274,7 +275,7 @@ def kv_attn_decode(q, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros, le
         ws, ws_bytes = None, 0
     else:
         if workspace is None:
-            need = kv_attn_decode_workspace(B, Hq, T, D)
+            need = kv_attn_decode_workspace(B, Hq, Hkv, T, D)
             workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
         ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
     st = library().qr_kv_attn_decode(_ptr(q), B, Hq, Hkv, T, D, _ptr(k_codes), _ptr(k_scales), _ptr(k_zeros),

@@ -123,10 +123,12 @@ qr_status qr_kv_quant(const void *kv_f16, int64_t T, int64_t H, int64_t head_dim
   return from_hip(qr::launch_kv_quant(kv_f16, T, H, ld_kv, signs, codes, scales, zeros, (hipStream_t)stream));
 }
 
-qr_status qr_kv_attn_decode_workspace(int64_t B, int64_t Hq, int64_t T, int64_t head_dim, int64_t *bytes) {
-  if (bytes == nullptr || B < 0 || Hq < 0 || T < 0) return QR_EINVAL;
+qr_status qr_kv_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t head_dim,
+                                      int64_t *bytes) {
+  if (bytes == nullptr || B < 0 || Hq < 0 || Hkv < 0 || T < 0) return QR_EINVAL;
   if (head_dim != 128) return QR_ESHAPE;
-  *bytes = qr::attn_decode_plan(B, Hq, T).workspace_bytes;
+  if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return QR_ESHAPE;
+  *bytes = qr::attn_decode_plan(B, Hq, Hkv, T).workspace_bytes;
   return QR_OK;
 }
 
@@ -150,12 +152,14 @@ qr_status qr_kv_attn_decode(const void *q_f16, int64_t B, int64_t Hq, int64_t Hk
   if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
     return QR_EALIGN;
   if ((lens != nullptr && !aligned(lens, 4)) || (signs != nullptr && !aligned(signs, 4))) return QR_EALIGN;
-  qr::AttnPlan plan = qr::attn_decode_plan(B, Hq, T);
+  qr::AttnPlan plan = qr::attn_decode_plan(B, Hq, Hkv, T);
   if (plan.splits > 1) {
     if (workspace == nullptr && workspace_bytes == 0) {
       // no workspace: one chunk per sequence
-      plan.chunk = T > 0 ? (T + 63) / 64 * 64 : 64;
+      plan.chunk = (T + 15) / 16 * 16;
       plan.splits = 1;
+      plan.tiles = B * plan.nhg;
+      plan.blocks = (plan.tiles + 7) / 8 * 8 * (Hq / Hkv);
       plan.workspace_bytes = 0;
     } else if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
       return QR_EINVAL;

@@ -14,14 +14,19 @@
 // and the value side accumulates sum_t w_t c_t - sum_t w_t z_t with
 // w_t = p_t D_t, all in fp32.
 //
-// Layout of the work: one block of four waves per (sequence, query head,
-// chunk of tokens).  Lane (tau, qd) = (lane >> 2, lane & 3) holds dims
-// 32 qd .. 32 qd + 31 of token tau of a 16-token step: its 16-byte quarter of
-// the token's 64-byte code row, so one load instruction reads 16 whole code
-// rows.  Online softmax per group of four steps (64 tokens per wave).  A
-// sequence split into several chunks leaves one partial (max, sum, 128
-// accumulators) per chunk in the caller's workspace; a second kernel merges
-// them.
+// Layout of the work: one block of four waves per (sequence, group of up to
+// eight KV heads, chunk of tokens, query head within a KV head's group).  A
+// 16-row step covers tps = 16 / hpg tokens of the group's hpg heads, whose
+// code rows are contiguous in the cache: lane (tau, qd) = (lane >> 2,
+// lane & 3) holds dims 32 qd .. 32 qd + 31 of head tau % hpg of token
+// tau / hpg, its 16-byte quarter of a 64-byte code row.  Every lane keeps its
+// own online-softmax state over its tokens (the four lanes of a row share
+// it); the lanes and waves are merged through LDS at the end.  A sequence
+// split into several chunks leaves one partial (max, sum, 128 accumulators)
+// per chunk and query head in the caller's workspace; a second kernel merges
+// them.  The query heads that share a KV head are placed on one XCD, one
+// after the other, so that they read the group's cache rows through the
+// same L2.
 #include "qr_common.h"
 #include "qr_launch.h"
 
@@ -31,7 +36,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kStep = 16;          // tokens per wave step
-constexpr int kGroup = 4;          // steps per online-softmax group
+constexpr int kGroup = 2;          // steps per online-softmax group
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
@@ -42,7 +47,8 @@ struct AttnArgs {
   const int *lens;                 // [B] or null
   const int8_t *signs;             // [128] or null
   float qmul;                      // sm_scale * log2(e) / sqrt(128)
-  int T, Hq, Hkv, group, chunk, splits;
+  int T, Hq, Hkv, G, nhg, chunk, splits;
+  int64_t U;                       // tiles: B * nhg * splits
   float *ws;                       // [B][Hq][splits][kPart] when splits > 1
   unsigned short *out;             // [B][Hq][128] fp16
 };
@@ -65,100 +71,110 @@ __device__ __forceinline__ unsigned short float_to_half(float f) {
 // In-place unnormalised 128-point Walsh-Hadamard transform of buf[0..127]
 // by threads 0..63 of the block (one butterfly pair each per level); every
 // thread of the block must call it.
-__device__ __forceinline__ void wht128_lds(float *buf) {
+// In-place unnormalised 128-point Walsh-Hadamard transform of rows
+// 0..nh-1 of buf (stride 128) by the whole block; every thread must call it.
+__device__ __forceinline__ void wht128_rows(float *buf, int nh) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int h = 1; h < kD; h <<= 1) {
     __syncthreads();
-    if (tid < kD / 2) {
-      const int i = (tid / h) * 2 * h + (tid % h);
-      const float a = buf[i], b = buf[i + h];
-      buf[i] = a + b;
-      buf[i + h] = a - b;
+    for (int p = tid; p < nh * (kD / 2); p += blockDim.x) {
+      const int row = p >> 6, j = p & 63;
+      float *r = buf + row * kD + (j / h) * 2 * h + (j % h);
+      const float x0 = r[0], x1 = r[h];
+      r[0] = x0 + x1;
+      r[h] = x0 - x1;
     }
   }
   __syncthreads();
 }
 
-// out = (o / l) R^T = WHT(o / l) * signs / sqrt(128), fp16; zeros when l == 0.
-// buf holds o on entry (threads 0..127 wrote it); every thread calls this.
-__device__ __forceinline__ void finish_output(float *buf, float l, const int8_t *signs, unsigned short *out) {
-  const int tid = threadIdx.x;
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  __syncthreads();
-  if (tid < kD) buf[tid] *= inv;
-  wht128_lds(buf);
-  if (tid < kD) {
-    float v = buf[tid] * 0.08838834764831845f;   // 1/sqrt(128)
-    if (signs != nullptr && signs[tid] < 0) v = -v;
-    out[tid] = float_to_half(v);
-  }
-}
+constexpr int kHG = 8;             // KV heads per block
+constexpr int kStage = 36;         // floats per lane in the merge stage: acc[32], m, l, pad
 
 __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
-  __shared__ float qbuf[kD];
-  __shared__ float wpart[kWaves][kD];
-  __shared__ float wml[kWaves][2];
-  __shared__ float qsum_s;
+  __shared__ __attribute__((aligned(16))) float qbuf[kHG * kD];
+  __shared__ __attribute__((aligned(16))) float stage[kWaves * 64 * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int s = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-  const int hk = hq / a.group;
   const int qd = lane & 3, tau = lane >> 2;
+
+  // block -> (tile u, query variant gi): the G variants of a tile are
+  // consecutive blocks of one XCD (blocks are dealt to the 8 XCDs in turn)
+  const int L = blockIdx.x;
+  const int k8 = L >> 3;
+  const int gi = k8 % a.G;
+  const int64_t u = (int64_t)(k8 / a.G) * 8 + (L & 7);
+  if (u >= a.U) return;
+  const int s = (int)(u % a.splits);
+  const int64_t bh = u / a.splits;
+  const int hg = (int)(bh % a.nhg);
+  const int b = (int)(bh / a.nhg);
+  const int h0 = hg * kHG;
+  const int hpg = a.Hkv - h0 < kHG ? a.Hkv - h0 : kHG;      // heads in this group, 1..8
+  const int tps = 16 / hpg;                                   // tokens per 16-row step
+  const int hh = tau % hpg;                                   // this lane's head in the group
+  const int toff = tau / hpg;                                 // and token within a step
+  const bool lane_ok = toff < tps;
 
   int len = a.lens != nullptr ? a.lens[b] : a.T;
   len = len < 0 ? 0 : (len > a.T ? a.T : len);
   const int t0 = s * a.chunk;
   const int t1 = t0 + a.chunk < len ? t0 + a.chunk : len;
 
-  // ---- q' = (q * signs) H_128 * qmul, and its sum
-  if (tid < kD) {
-    float v = half_to_float(a.q[((int64_t)b * a.Hq + hq) * kD + tid]);
-    if (a.signs != nullptr && a.signs[tid] < 0) v = -v;
-    qbuf[tid] = v;
+  // ---- q' = (q * signs) H_128 * qmul for the group's query heads
+  for (int p = tid; p < hpg * kD; p += 64 * kWaves) {
+    const int r = p >> 7, d = p & 127;
+    const int hq = (h0 + r) * a.G + gi;
+    float v = half_to_float(a.q[((int64_t)b * a.Hq + hq) * kD + d]);
+    if (a.signs != nullptr && a.signs[d] < 0) v = -v;
+    qbuf[p] = v;
   }
-  wht128_lds(qbuf);
-  if (tid < 64) {
-    float v = (qbuf[2 * tid] + qbuf[2 * tid + 1]) * a.qmul;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    if (tid == 0) qsum_s = v;
-  }
-  __syncthreads();
+  wht128_rows(qbuf, hpg);
   float qv[32];
+  float qsum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) qv[i] = qbuf[32 * qd + i] * a.qmul;
-  const float qsum = qsum_s;
+  for (int i = 0; i < 32; ++i) {
+    qv[i] = qbuf[hh * kD + 32 * qd + i] * a.qmul;
+    qsum += qv[i];
+  }
+  qsum += dpp<kQuadXor1>(qsum);
+  qsum += dpp<kQuadXor2>(qsum);
 
-  // ---- this wave's tokens: steps j with token base t0 + (j * kWaves + wave) * kStep
-  const int64_t tok_stride = (int64_t)a.Hkv;                  // rows of 64 bytes between tokens
-  const int64_t seq_row0 = (int64_t)b * a.T * a.Hkv + hk;      // row index of token 0
   float m = -__builtin_inff();
   float l = 0.f, zacc = 0.f;
   float acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = 0.f;
 
-  const int nsteps = (t1 - t0 + kStep - 1) / kStep;            // over the block; t1 <= t0 gives <= 0
-  for (int j0 = wave; j0 < nsteps; j0 += kWaves * kGroup) {
+  const int64_t head_row = h0 + hh;                            // + (b T + t) Hkv
+  const int nsteps = t1 > t0 ? (t1 - t0 + tps - 1) / tps : 0;
+
+  // one online-softmax group: kGroup steps of this wave, loaded one group
+  // ahead of the arithmetic
+  struct Grp {
     v4u kw[kGroup], vw[kGroup];
     float kd[kGroup], vd[kGroup], kzf[kGroup], vzf[kGroup];
     bool ok[kGroup];
+  };
+  auto load = [&](int j0, Grp &G) __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      const int t = t0 + (j0 + g * kWaves) * kStep + tau;
-      ok[g] = t < t1;
-      const int tc = ok[g] ? t : t1 - 1;                       // in-range row for masked lanes
-      const int64_t row = seq_row0 + (int64_t)tc * tok_stride;
-      kw[g] = *(const v4u *)(a.kc + row * 64 + 16 * qd);
-      vw[g] = *(const v4u *)(a.vc + row * 64 + 16 * qd);
-      kd[g] = a.ks[row];
-      vd[g] = a.vs[row];
-      kzf[g] = (float)a.kz[row];
-      vzf[g] = (float)a.vz[row];
+      const int t = t0 + (j0 + g * kWaves) * tps + toff;
+      G.ok[g] = lane_ok && t < t1;
+      const int tc = G.ok[g] ? t : t0;                         // an in-range row for masked lanes
+      const int64_t row = ((int64_t)b * a.T + tc) * a.Hkv + head_row;
+      G.kw[g] = *(const v4u *)(a.kc + row * 64 + 16 * qd);
+      G.vw[g] = *(const v4u *)(a.vc + row * 64 + 16 * qd);
+      G.kd[g] = a.ks[row];
+      G.vd[g] = a.vs[row];
+      G.kzf[g] = (float)a.kz[row];
+      G.vzf[g] = (float)a.vz[row];
     }
+  };
+  auto compute = [&](const Grp &G) __attribute__((always_inline)) {
     float sc[kGroup];
     float gmax = -__builtin_inff();
 #pragma unroll
@@ -166,7 +182,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
       float dot = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        unsigned lo = kw[g][w] & 0x0F0F0F0Fu, hi = (kw[g][w] >> 4) & 0x0F0F0F0Fu;
+        unsigned lo = G.kw[g][w] & 0x0F0F0F0Fu, hi = (G.kw[g][w] >> 4) & 0x0F0F0F0Fu;
         opaque(lo);
         opaque(hi);
 #pragma unroll
@@ -177,10 +193,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
       }
       dot += dpp<kQuadXor1>(dot);
       dot += dpp<kQuadXor2>(dot);
-      sc[g] = ok[g] ? kd[g] * (dot - kzf[g] * qsum) : -__builtin_inff();
+      sc[g] = G.ok[g] ? G.kd[g] * (dot - G.kzf[g] * qsum) : -__builtin_inff();
       gmax = fmaxf(gmax, sc[g]);
     }
-    gmax = wave_max_dpp(gmax);
     const float m_new = fmaxf(m, gmax);
     const float m_ref = m_new == -__builtin_inff() ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
@@ -193,11 +208,11 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
     for (int g = 0; g < kGroup; ++g) {
       const float p = __builtin_amdgcn_exp2f(sc[g] - m_ref);
       l += p;
-      const float w8 = p * vd[g];
-      zacc = __builtin_fmaf(w8, vzf[g], zacc);
+      const float w8 = p * G.vd[g];
+      zacc = __builtin_fmaf(w8, G.vzf[g], zacc);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        unsigned lo = vw[g][w] & 0x0F0F0F0Fu, hi = (vw[g][w] >> 4) & 0x0F0F0F0Fu;
+        unsigned lo = G.vw[g][w] & 0x0F0F0F0Fu, hi = (G.vw[g][w] >> 4) & 0x0F0F0F0Fu;
         opaque(lo);
         opaque(hi);
 #pragma unroll
@@ -207,96 +222,151 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
         }
       }
     }
+  };
+
+  constexpr int kAdv = kWaves * kGroup;                          // steps between a wave's groups
+  Grp ga, gb;
+  int j = wave;
+  if (j < nsteps) load(j, ga);
+  while (j < nsteps) {
+    const int jb = j + kAdv;
+    if (jb < nsteps) load(jb, gb);
+    compute(ga);
+    if (jb >= nsteps) break;
+    const int jc = jb + kAdv;
+    if (jc < nsteps) load(jc, ga);
+    compute(gb);
+    j = jc;
   }
 
-  // ---- per wave: subtract the zero-point term, sum over the 16 tokens of a step
+  // ---- stage every lane's state: acc - zacc (the zero-point term), m, l
+  float *st = stage + (wave * 64 + lane) * kStage;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float v = acc[i] - zacc;
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    acc[i] = v;
-  }
-  // l is the same in the four lanes of a token: sum one lane per token
-  float lw = qd == 0 ? l : 0.f;
-#pragma unroll
-  for (int o = 4; o <= 32; o <<= 1) lw += __shfl_xor(lw, o);
-  if (tau == 0) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) wpart[wave][32 * qd + i] = acc[i];
-  }
-  if (lane == 0) {
-    wml[wave][0] = m;
-    wml[wave][1] = lw;
-  }
+  for (int i = 0; i < 32; i += 4)
+    *(v4f *)(st + i) = v4f{acc[i] - zacc, acc[i + 1] - zacc, acc[i + 2] - zacc, acc[i + 3] - zacc};
+  st[32] = m;
+  st[33] = l;
   __syncthreads();
 
-  // ---- merge the four waves
-  float mb = -__builtin_inff();
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) mb = fmaxf(mb, wml[w][0]);
-  const float mref = mb == -__builtin_inff() ? 0.f : mb;
-  float lb = 0.f, ob = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float f = __builtin_amdgcn_exp2f(wml[w][0] - mref);
-    lb += f * wml[w][1];
-    if (tid < kD) ob += f * wpart[w][tid];
+  // ---- merge per (head, dim) over the waves and the tokens of a step
+  for (int p = tid; p < hpg * kD; p += 64 * kWaves) {
+    const int r = p >> 7, d = p & 127;
+    const int dq = d >> 5, di = d & 31;
+    float mb = -__builtin_inff();
+    for (int w = 0; w < kWaves; ++w)
+      for (int to = 0; to < tps; ++to) mb = fmaxf(mb, stage[(w * 64 + 4 * (to * hpg + r) + dq) * kStage + 32]);
+    const float mref = mb == -__builtin_inff() ? 0.f : mb;
+    float lb = 0.f, ob = 0.f;
+    for (int w = 0; w < kWaves; ++w)
+      for (int to = 0; to < tps; ++to) {
+        const float *e = stage + (w * 64 + 4 * (to * hpg + r) + dq) * kStage;
+        const float f = __builtin_amdgcn_exp2f(e[32] - mref);
+        lb += f * e[33];
+        ob += f * e[di];
+      }
+    const int hq = (h0 + r) * a.G + gi;
+    if (a.splits == 1) {
+      qbuf[p] = lb > 0.f ? ob / lb : 0.f;
+    } else {
+      float *part = a.ws + (((int64_t)b * a.Hq + hq) * a.splits + s) * kPart;
+      part[4 + d] = ob;
+      if (d == 0) {
+        part[0] = mb;
+        part[1] = lb;
+      }
+    }
   }
   if (a.splits == 1) {
-    if (tid < kD) qbuf[tid] = ob;
-    finish_output(qbuf, lb, a.signs, a.out + ((int64_t)b * a.Hq + hq) * kD);
-  } else {
-    float *part = a.ws + (((int64_t)b * a.Hq + hq) * a.splits + s) * kPart;
-    if (tid < kD) part[4 + tid] = ob;
-    if (tid == 0) {
-      part[0] = mb;
-      part[1] = lb;
+    // out = o R^T: transform, then signs and 1/sqrt(128)
+    wht128_rows(qbuf, hpg);
+    for (int p = tid; p < hpg * kD; p += 64 * kWaves) {
+      const int r = p >> 7, d = p & 127;
+      const int hq = (h0 + r) * a.G + gi;
+      float v = qbuf[p] * 0.08838834764831845f;
+      if (a.signs != nullptr && a.signs[d] < 0) v = -v;
+      a.out[((int64_t)b * a.Hq + hq) * kD + d] = float_to_half(v);
     }
   }
 }
 
-// Merge the chunks of one (sequence, query head): max, rescaled sums, output.
-__global__ __launch_bounds__(kD) void attn_combine_kernel(AttnArgs a) {
+constexpr int kMaxSplits = 2048;   // the plan never splits a sequence further
+
+// Merge the chunks of one (sequence, query head): block-wide max of the
+// chunk maxima, their weights in LDS, then each half of the block sums every
+// other chunk's accumulators (independent loads, many in flight), output.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float fs[kMaxSplits];
+  __shared__ float red[2][4];
+  __shared__ float half_o[kD];
   __shared__ float buf[kD];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hq = blockIdx.x, b = blockIdx.y;
-  const float *part = a.ws + ((int64_t)b * a.Hq + hq) * a.splits * kPart;
-  float mb = -__builtin_inff();
-  for (int s = 0; s < a.splits; ++s) mb = fmaxf(mb, part[s * kPart]);
+  const int S = a.splits;
+  const float *part = a.ws + ((int64_t)b * a.Hq + hq) * S * kPart;
+
+  float mloc = -__builtin_inff();
+  for (int s = tid; s < S; s += 256) mloc = fmaxf(mloc, part[s * kPart]);
+  mloc = wave_max_dpp(mloc);
+  if (lane == 0) red[0][wave] = mloc;
+  __syncthreads();
+  const float mb = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
   const float mref = mb == -__builtin_inff() ? 0.f : mb;
-  float lb = 0.f, ob = 0.f;
-  for (int s = 0; s < a.splits; ++s) {
+  float lloc = 0.f;
+  for (int s = tid; s < S; s += 256) {
     const float f = __builtin_amdgcn_exp2f(part[s * kPart] - mref);
-    lb += f * part[s * kPart + 1];
-    ob += f * part[s * kPart + 4 + tid];
+    fs[s] = f;
+    lloc += f * part[s * kPart + 1];
   }
-  buf[tid] = ob;
-  finish_output(buf, lb, a.signs, a.out + ((int64_t)b * a.Hq + hq) * kD);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lloc += __shfl_xor(lloc, o);
+  if (lane == 0) red[1][wave] = lloc;
+  __syncthreads();
+  const float lb = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+
+  const int d = tid & (kD - 1), h = tid >> 7;
+  float o0 = 0.f, o1 = 0.f;
+  int s = h;
+#pragma unroll 4
+  for (; s + 2 < S; s += 4) {
+    o0 += fs[s] * part[s * kPart + 4 + d];
+    o1 += fs[s + 2] * part[(s + 2) * kPart + 4 + d];
+  }
+  if (s < S) o0 += fs[s] * part[s * kPart + 4 + d];
+  if (h == 1) half_o[d] = o0 + o1;
+  __syncthreads();
+  if (h == 0) buf[d] = lb > 0.f ? (o0 + o1 + half_o[d]) / lb : 0.f;
+  wht128_rows(buf, 1);
+  if (h == 0) {
+    float v = buf[d] * 0.08838834764831845f;
+    if (a.signs != nullptr && a.signs[d] < 0) v = -v;
+    a.out[((int64_t)b * a.Hq + hq) * kD + d] = float_to_half(v);
+  }
 }
 
 }  // namespace
 
-AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t T) {
-  const int64_t cus = 256;   // the split depends on the shape only, not on the device
+AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t T) {
   AttnPlan p{};
-  const int64_t pairs = B * Hq;
+  const int64_t nhg = Hkv > 0 ? (Hkv + kHG - 1) / kHG : 0;
+  const int64_t G = Hkv > 0 ? Hq / Hkv : 0;
+  const int64_t base = B * nhg * G;                              // blocks without splitting
   int64_t splits = 1;
-  if (T > 256 && pairs > 0) {
-    const int64_t want = (8LL * cus + pairs - 1) / pairs;          // about eight blocks per CU
-    const int64_t most = (T + 255) / 256;                            // chunks of at least 256 tokens
+  if (T > 64 && base > 0) {
+    const int64_t want = (2048 + base - 1) / base;               // about eight blocks per CU of 256;
+                                                                 // at most kMaxSplits
+    const int64_t most = (T + 63) / 64;                          // chunks of at least 64 tokens
     splits = want < most ? want : most;
-    if (splits < 1) splits = 1;
   }
   int64_t chunk = (T + splits - 1) / splits;
-  chunk = (chunk + 63) / 64 * 64;
-  if (chunk < 64) chunk = 64;
+  chunk = (chunk + 15) / 16 * 16;
+  if (chunk < 16) chunk = 16;
   p.chunk = chunk;
   p.splits = (T + chunk - 1) / chunk;
   if (p.splits < 1) p.splits = 1;
-  p.workspace_bytes = p.splits > 1 ? pairs * p.splits * kPart * (int64_t)sizeof(float) : 0;
+  p.nhg = nhg;
+  p.tiles = B * nhg * p.splits;
+  p.blocks = (p.tiles + 7) / 8 * 8 * G;
+  p.workspace_bytes = p.splits > 1 ? B * Hq * p.splits * kPart * (int64_t)sizeof(float) : 0;
   return p;
 }
 
@@ -318,15 +388,17 @@ hipError_t launch_attn_decode(const void *q, int64_t B, int64_t Hq, int64_t Hkv,
   a.T = (int)T;
   a.Hq = (int)Hq;
   a.Hkv = (int)Hkv;
-  a.group = (int)(Hq / Hkv);
+  a.G = (int)(Hq / Hkv);
+  a.nhg = (int)plan.nhg;
+  a.U = plan.tiles;
   a.chunk = (int)plan.chunk;
   a.splits = (int)plan.splits;
   a.ws = ws;
   a.out = (unsigned short *)out;
-  attn_decode_kernel<<<dim3((unsigned)plan.splits, (unsigned)Hq, (unsigned)B), dim3(64 * kWaves), 0, stream>>>(a);
+  attn_decode_kernel<<<dim3((unsigned)plan.blocks), dim3(64 * kWaves), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  attn_combine_kernel<<<dim3((unsigned)Hq, (unsigned)B), dim3(kD), 0, stream>>>(a);
+  attn_combine_kernel<<<dim3((unsigned)Hq, (unsigned)B), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -50,11 +50,14 @@ hipError_t launch_gemm_decode(const uint8_t *a, const float *sa, const uint8_t *
 // (tokens per chunk, chunks per sequence, workspace size) depends on the
 // shape only.
 struct AttnPlan {
-  int64_t chunk;
-  int64_t splits;
+  int64_t chunk;            // tokens per chunk
+  int64_t splits;           // chunks per sequence
+  int64_t nhg;              // groups of up to eight KV heads
+  int64_t tiles;            // B * nhg * splits
+  int64_t blocks;           // grid size
   int64_t workspace_bytes;
 };
-AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t T);
+AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t T);
 hipError_t launch_attn_decode(const void *q, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, const uint8_t *kc,
                               const float *ks, const uint8_t *kz, const uint8_t *vc, const float *vs,
                               const uint8_t *vz, const int *lens, const int8_t *signs, float sm_scale,

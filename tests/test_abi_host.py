@@ -181,14 +181,19 @@ def test_attn_empty_batch_is_noop():
 
 
 def test_attn_workspace_size():
-    """One decode query per head over 4096 tokens is split into 16 chunks of
-    256 tokens (32 heads x 16 partials of 132 floats); a 64-sequence batch
-    fills the chip without splitting and needs none."""
-    assert qr.kv_attn_decode_workspace(1, 32, 4096) == 32 * 16 * 132 * 4
-    assert qr.kv_attn_decode_workspace(64, 32, 2048) == 0
-    assert qr.kv_attn_decode_workspace(4, 32, 100) == 0
+    """Blocks take up to eight KV heads; a shape with fewer than 2048 such
+    blocks is split into chunks of at least 64 tokens, each chunk leaving a
+    partial of 132 floats per query head.  One query per head over 4096
+    tokens: 4 head groups -> 64 chunks.  64 sequences x 2048 tokens: 256
+    head groups -> 8 chunks.  64 tokens or fewer are never split."""
+    assert qr.kv_attn_decode_workspace(1, 32, 32, 4096) == 32 * 64 * 132 * 4
+    assert qr.kv_attn_decode_workspace(64, 32, 32, 2048) == 64 * 32 * 8 * 132 * 4
+    assert qr.kv_attn_decode_workspace(64, 64, 8, 2048) == 64 * 64 * 4 * 132 * 4
+    assert qr.kv_attn_decode_workspace(4, 32, 32, 64) == 0
     with pytest.raises(qr.QRError):
-        qr.kv_attn_decode_workspace(1, 32, 4096, head_dim=64)
+        qr.kv_attn_decode_workspace(1, 32, 32, 4096, head_dim=64)
+    with pytest.raises(qr.QRError):
+        qr.kv_attn_decode_workspace(1, 32, 5, 4096)
     out = ctypes.c_int64(0)
-    assert qr.library().qr_kv_attn_decode_workspace(1, 32, -1, 128, ctypes.byref(out)) == qr.QR_EINVAL
-    assert qr.library().qr_kv_attn_decode_workspace(1, 32, 1, 128, None) == qr.QR_EINVAL
+    assert qr.library().qr_kv_attn_decode_workspace(1, 32, 32, -1, 128, ctypes.byref(out)) == qr.QR_EINVAL
+    assert qr.library().qr_kv_attn_decode_workspace(1, 32, 32, 1, 128, None) == qr.QR_EINVAL

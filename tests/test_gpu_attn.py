@@ -59,7 +59,7 @@ def test_attn_lens_signs_scale(qr):
     lens = np.array([0, 1, 257, 1499, 1500], np.int32)
     signs = np.where(np.random.default_rng(13).random(128) < 0.5, -1, 1).astype(np.int8)
     want = oracle(q, cache, lens=lens, signs=signs, sm_scale=0.15)
-    assert qr.kv_attn_decode_workspace(B, Hq, T) > 0
+    assert qr.kv_attn_decode_workspace(B, Hq, Hkv, T) > 0
     got = run(qr, q, cache, lens=lens, signs=signs, sm_scale=0.15)
     check_attn(got, want)
     assert np.all(got[0] == 0)
