@@ -11,8 +11,9 @@
 // the query is rotated once, the cache is used as stored, and the output is
 // rotated back once.  Per token:
 //   score = D (q' . c - z sum(q')),   q' = q R * sm_scale * log2(e)
-// and the value side accumulates sum_t w_t c_t - sum_t w_t z_t with
-// w_t = p_t D_t, all in fp32.
+// with q' . c on v_dot4_i32_i8 against q' split into three int8 parts (as
+// exact as fp32), and the value side accumulates sum_t w_t c_t - sum_t w_t z_t
+// with w_t = p_t D_t in fp32 (v_fma_mix on the codes read as fp16).
 //
 // Layout of the work: one block of four waves per (sequence, group of up to
 // eight KV heads, chunk of tokens, query head within a KV head's group).  A
@@ -55,10 +56,8 @@ struct AttnArgs {
 
 constexpr int kPart = 132;         // m, l, 2 pad, o[128]
 
-// Hides a value's known bits from the optimiser, so that byte k of a masked
-// word converts with one v_cvt_f32_ubyte<k> instead of a bit-field extract
-// followed by a conversion.
-__device__ __forceinline__ void opaque(unsigned &v) { asm volatile("" : "+v"(v)); }
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float half_to_float(unsigned short h) {
   return (float)__builtin_bit_cast(_Float16, h);
@@ -90,7 +89,7 @@ __device__ __forceinline__ void wht128_rows(float *buf, int nh) {
 }
 
 constexpr int kHG = 8;             // KV heads per block
-constexpr int kStage = 36;         // floats per lane in the merge stage: acc[32], m, l, pad
+constexpr int kStage = 34;         // floats per lane in the merge stage: acc[32], m, l
 
 __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float qbuf[kHG * kD];
@@ -124,24 +123,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
   const int t0 = s * a.chunk;
   const int t1 = t0 + a.chunk < len ? t0 + a.chunk : len;
 
-  // ---- q' = (q * signs) H_128 * qmul for the group's query heads
-  for (int p = tid; p < hpg * kD; p += 64 * kWaves) {
-    const int r = p >> 7, d = p & 127;
-    const int hq = (h0 + r) * a.G + gi;
-    float v = half_to_float(a.q[((int64_t)b * a.Hq + hq) * kD + d]);
-    if (a.signs != nullptr && a.signs[d] < 0) v = -v;
-    qbuf[p] = v;
-  }
-  wht128_rows(qbuf, hpg);
-  float qv[32];
+  unsigned qe[3][4], qo[3][4];   // the query in int8 parts, filled below
+  float qscale[3];
   float qsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    qv[i] = qbuf[hh * kD + 32 * qd + i] * a.qmul;
-    qsum += qv[i];
-  }
-  qsum += dpp<kQuadXor1>(qsum);
-  qsum += dpp<kQuadXor2>(qsum);
 
   float m = -__builtin_inff();
   float l = 0.f, zacc = 0.f;
@@ -179,18 +163,19 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
     float gmax = -__builtin_inff();
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      float dot = 0.f;
+      // q' . c on the int8 dot product: codes are bytes 0..15 after masking
+      int d0 = 0, d1 = 0, d2 = 0;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         unsigned lo = G.kw[g][w] & 0x0F0F0F0Fu, hi = (G.kw[g][w] >> 4) & 0x0F0F0F0Fu;
-        opaque(lo);
-        opaque(hi);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          dot = __builtin_fmaf(qv[8 * w + 2 * k], (float)((lo >> (8 * k)) & 0xFFu), dot);
-          dot = __builtin_fmaf(qv[8 * w + 2 * k + 1], (float)((hi >> (8 * k)) & 0xFFu), dot);
-        }
+        d0 = __builtin_amdgcn_sdot4((int)lo, (int)qe[0][w], d0, false);
+        d0 = __builtin_amdgcn_sdot4((int)hi, (int)qo[0][w], d0, false);
+        d1 = __builtin_amdgcn_sdot4((int)lo, (int)qe[1][w], d1, false);
+        d1 = __builtin_amdgcn_sdot4((int)hi, (int)qo[1][w], d1, false);
+        d2 = __builtin_amdgcn_sdot4((int)lo, (int)qe[2][w], d2, false);
+        d2 = __builtin_amdgcn_sdot4((int)hi, (int)qo[2][w], d2, false);
       }
+      float dot = __builtin_fmaf(qscale[0], (float)d0, __builtin_fmaf(qscale[1], (float)d1, qscale[2] * (float)d2));
       dot += dpp<kQuadXor1>(dot);
       dot += dpp<kQuadXor2>(dot);
       sc[g] = G.ok[g] ? G.kd[g] * (dot - G.kzf[g] * qsum) : -__builtin_inff();
@@ -198,27 +183,33 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
     }
     const float m_new = fmaxf(m, gmax);
     const float m_ref = m_new == -__builtin_inff() ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
-    m = m_new;
-    l *= alpha;
-    zacc *= alpha;
+    if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {          // rescale only when a max moved
+      const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
+      l *= alpha;
+      zacc *= alpha;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+      for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+    }
+    m = m_new;
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
       const float p = __builtin_amdgcn_exp2f(sc[g] - m_ref);
       l += p;
       const float w8 = p * G.vd[g];
       zacc = __builtin_fmaf(w8, G.vzf[g], zacc);
+      // A masked nibble n read as an fp16 is the subnormal n 2^-24, exact in
+      // v_fma_mix's conversion; the weight carries the 2^24.
+      const float w24 = w8 * 16777216.0f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        unsigned lo = G.vw[g][w] & 0x0F0F0F0Fu, hi = (G.vw[g][w] >> 4) & 0x0F0F0F0Fu;
-        opaque(lo);
-        opaque(hi);
+        const unsigned v = G.vw[g][w];
+        h2 e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) e[k] = __builtin_bit_cast(h2, (v >> (4 * k)) & 0x000F000Fu);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          acc[8 * w + 2 * k] = __builtin_fmaf(w8, (float)((lo >> (8 * k)) & 0xFFu), acc[8 * w + 2 * k]);
-          acc[8 * w + 2 * k + 1] = __builtin_fmaf(w8, (float)((hi >> (8 * k)) & 0xFFu), acc[8 * w + 2 * k + 1]);
+          acc[8 * w + k] = __builtin_fmaf(w24, (float)e[k][0], acc[8 * w + k]);
+          acc[8 * w + 4 + k] = __builtin_fmaf(w24, (float)e[k][1], acc[8 * w + 4 + k]);
         }
       }
     }
@@ -227,7 +218,58 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
   constexpr int kAdv = kWaves * kGroup;                          // steps between a wave's groups
   Grp ga, gb;
   int j = wave;
-  if (j < nsteps) load(j, ga);
+  if (j < nsteps) load(j, ga);     // in flight while the query is prepared
+
+  // ---- q' = (q * signs) H_128 * qmul for the group's query heads
+  for (int p = tid; p < hpg * kD; p += 64 * kWaves) {
+    const int r = p >> 7, d = p & 127;
+    const int hq = (h0 + r) * a.G + gi;
+    float v = half_to_float(a.q[((int64_t)b * a.Hq + hq) * kD + d]);
+    if (a.signs != nullptr && a.signs[d] < 0) v = -v;
+    qbuf[p] = v;
+  }
+  wht128_rows(qbuf, hpg);
+  // The lane's 32 query values as three int8 parts, q' ~ s1 p1 + s2 p2 + s3 p3
+  // with |p| <= 127 and s_{k+1} = s_k / 254 (each remainder is at most half a
+  // step, so the next part fits; the last remainder is below 2^-23 of the
+  // lane's max |q'|).  Part bytes are laid out as the code bytes: word w of
+  // qe holds dims 8w, 8w+2, 8w+4, 8w+6 (the low nibbles of a code word),
+  // qo dims 8w+1, ..., 8w+7 (the high nibbles).
+  {
+    float qv[32];
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      qv[i] = qbuf[hh * kD + 32 * qd + i] * a.qmul;
+      qsum += qv[i];
+      mx = fmaxf(mx, fabsf(qv[i]));
+    }
+    float sc = mx > 0.f ? mx / 127.0f : 1.0f;
+#pragma unroll
+    for (int part = 0; part < 3; ++part) {
+      const float inv = 1.0f / sc;
+      qscale[part] = sc;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        unsigned e = 0u, o = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float ve = __builtin_rintf(qv[8 * w + 2 * k] * inv);
+          const float vo = __builtin_rintf(qv[8 * w + 2 * k + 1] * inv);
+          qv[8 * w + 2 * k] = __builtin_fmaf(-ve, sc, qv[8 * w + 2 * k]);
+          qv[8 * w + 2 * k + 1] = __builtin_fmaf(-vo, sc, qv[8 * w + 2 * k + 1]);
+          e |= ((unsigned)(int)ve & 0xFFu) << (8 * k);
+          o |= ((unsigned)(int)vo & 0xFFu) << (8 * k);
+        }
+        qe[part][w] = e;
+        qo[part][w] = o;
+      }
+      sc *= 1.0f / 254.0f;
+    }
+  }
+  qsum += dpp<kQuadXor1>(qsum);
+  qsum += dpp<kQuadXor2>(qsum);
+
   while (j < nsteps) {
     const int jb = j + kAdv;
     if (jb < nsteps) load(jb, gb);
@@ -242,10 +284,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
   // ---- stage every lane's state: acc - zacc (the zero-point term), m, l
   float *st = stage + (wave * 64 + lane) * kStage;
 #pragma unroll
-  for (int i = 0; i < 32; i += 4)
-    *(v4f *)(st + i) = v4f{acc[i] - zacc, acc[i + 1] - zacc, acc[i + 2] - zacc, acc[i + 3] - zacc};
-  st[32] = m;
-  st[33] = l;
+  for (int i = 0; i < 32; i += 2) *(v2f *)(st + i) = v2f{acc[i] - zacc, acc[i + 1] - zacc};
+  *(v2f *)(st + 32) = v2f{m, l};
   __syncthreads();
 
   // ---- merge per (head, dim) over the waves and the tokens of a step
@@ -352,7 +392,7 @@ AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t T) {
   const int64_t base = B * nhg * G;                              // blocks without splitting
   int64_t splits = 1;
   if (T > 64 && base > 0) {
-    const int64_t want = (2048 + base - 1) / base;               // about eight blocks per CU of 256;
+    const int64_t want = (1024 + base - 1) / base;               // about four blocks per CU of 256;
                                                                  // at most kMaxSplits
     const int64_t most = (T + 63) / 64;                          // chunks of at least 64 tokens
     splits = want < most ? want : most;
