@@ -45,7 +45,7 @@ Readings where the pages are silent (each repeated where it is used):
      step = 0, z = 0, q = 0.
   R13 Output dequantization in fp64: y = acc * s_x * s_w, or for groups the sum
      over groups of acc_g * s_x[g] * s_w[g].
-  R14 Decode attention over the 4-bit KV cache: the query stays in full
+  R19 Decode attention over the 4-bit KV cache: the query stays in full
      precision, keys and values are the dequantized cache rotated back to the
      original basis, softmax is unquantized; out = softmax(c q K^T) V over the
      first len tokens of the sequence, query head h reading KV head
@@ -349,7 +349,7 @@ def kv_dequantize(q, step, z) -> np.ndarray:
 
 def kv_attention_decode(q, k_codes, k_step, k_zero, v_codes, v_step, v_zero, lens=None, signs=None,
                         sm_scale=None):
-    """One decode step of attention reading the rotated 4-bit KV cache (R14).
+    """One decode step of attention reading the rotated 4-bit KV cache (R19).
 
     [QuaRot-abs]: computational invariance applied to the attention mechanism
     and the KV cache, the cache held in 4 bits.  [DuQuant] Knowl 12: the
