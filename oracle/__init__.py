@@ -50,6 +50,9 @@ Readings where the pages are silent (each repeated where it is used):
      original basis, softmax is unquantized; out = softmax(c q K^T) V over the
      first len tokens of the sequence, query head h reading KV head
      h // (Hq / Hkv); an empty sequence gives zeros.
+  R20 6- and 8-bit variants: the same symmetric RTN with qmax = 2^(b-1) - 1
+     (31, 127) in place of 7; codes stored one per byte (int8) and multiplied
+     as int8, no packing.
 """
 from __future__ import annotations
 
@@ -175,17 +178,21 @@ def rotate_kron(x, had_n: int, dense, signs=None) -> np.ndarray:
 # Symmetric round-to-nearest 4-bit quantization and nibble packing
 # --------------------------------------------------------------------------
 
-def quantize_symmetric(y: np.ndarray, group: int = 0):
-    """Symmetric 4-bit RTN of each row of y (group 0) or of each contiguous
+def quantize_symmetric(y: np.ndarray, group: int = 0, bits: int = 4):
+    """Symmetric b-bit RTN of each row of y (group 0) or of each contiguous
     ``group``-block of a row.  [QuaRot-sum] Key points: activations quantized
     on the fly with round-to-nearest; group size 128 as the group-wise option.
+    [QuaRot-abs]: plain round-to-nearest at 6 and 8 bits as well (R20).
 
     Returns (codes int8 [rows, n], scales fp64 [rows] or [rows, n/group],
-    pre-rounding values y/s as fp64 [rows, n]).
-      s = max|y| / 7                 (R4; the group maximum maps to +-7)
-      q = clip(rint(y / s), -8, 7)   (R5)
-      max|y| = 0  ->  s = 0, q = 0   (R6)
+    pre-rounding values y/s as fp64 [rows, n]).  With qmax = 2^(b-1) - 1:
+      s = max|y| / qmax                     (R4; the group maximum maps to +-qmax)
+      q = clip(rint(y / s), -qmax-1, qmax)  (R5)
+      max|y| = 0  ->  s = 0, q = 0          (R6)
     """
+    if bits not in (4, 6, 8):
+        raise ValueError("bits must be 4, 6 or 8")
+    qmax = 2 ** (bits - 1) - 1
     y = np.asarray(y, dtype=np.float64)
     rows, n = y.shape
     g = n if group == 0 else group
@@ -193,11 +200,11 @@ def quantize_symmetric(y: np.ndarray, group: int = 0):
         raise ValueError("group must divide the row width")
     yg = y.reshape(rows, n // g, g)
     amax = np.abs(yg).max(axis=2)
-    s = amax / 7.0
+    s = amax / qmax
     t = np.zeros_like(yg)
     nz = s > 0
     t[nz] = yg[nz] / s[nz][:, None]
-    q = np.clip(np.rint(t), -8, 7).astype(np.int8)
+    q = np.clip(np.rint(t), -qmax - 1, qmax).astype(np.int8)
     scales = s[:, 0] if group == 0 else s
     return q.reshape(rows, n), scales, t.reshape(rows, n)
 
@@ -245,14 +252,15 @@ def rotate_weights(w, r: np.ndarray) -> np.ndarray:
     return r.T @ np.asarray(w).astype(np.float64)
 
 
-def quantize_weights(w_rot: np.ndarray, group: int = 0):
+def quantize_weights(w_rot: np.ndarray, group: int = 0, bits: int = 4):
     """Symmetric RTN of each output channel (column of W'), or of each
     ``group``-block of it along K (R4, R9).  [QuaRot-sum] Key points: RTN as the
-    4-bit weight quantizer next to GPTQ (the RTN-GPTQ gap).
+    4-bit weight quantizer next to GPTQ (the RTN-GPTQ gap); [QuaRot-abs]: RTN
+    at 6 and 8 bits (R20).
 
     Returns (codes int8 [N, K], scales fp64 [N] or [N, K/group]) in the
     output-channel-major layout the GEMM consumes."""
-    q, s, _ = quantize_symmetric(np.asarray(w_rot, dtype=np.float64).T, group)
+    q, s, _ = quantize_symmetric(np.asarray(w_rot, dtype=np.float64).T, group, bits)
     return q, s
 
 
@@ -291,13 +299,14 @@ def dequantize_output(acc: np.ndarray, sx: np.ndarray, sw: np.ndarray, group: in
     return y
 
 
-def linear_w4a4(x, w, r: np.ndarray, group: int = 0):
+def linear_w4a4(x, w, r: np.ndarray, group: int = 0, bits: int = 4):
     """The whole layer as the oracle computes it: rotate x, quantize it, rotate
-    and quantize W offline, integer GEMM, fp64 dequantization.  Returns a dict
-    with every intermediate."""
+    and quantize W offline, integer GEMM, fp64 dequantization (4-bit by
+    default; ``bits`` 6 or 8 for the R20 variants).  Returns a dict with every
+    intermediate."""
     y = rotate(x, r)
-    qx, sx, tx = quantize_symmetric(y, group)
-    qw, sw = quantize_weights(rotate_weights(w, r), group)
+    qx, sx, tx = quantize_symmetric(y, group, bits)
+    qw, sw = quantize_weights(rotate_weights(w, r), group, bits)
     acc = int_gemm(qx, qw, group)
     out = dequantize_output(acc, sx, sw, group)
     return dict(y=y, qx=qx, sx=sx, tx=tx, qw=qw, sw=sw, acc=acc, out=out)

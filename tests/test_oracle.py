@@ -544,3 +544,62 @@ def test_attn_rotated_domain_identity():
         want[0, h] = (p / p.sum()) @ vrot[0, :, h // 4] @ r.T
     got = O.kv_attention_decode(q, kc, ks, kz, vc, vs, vz, signs=signs)
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------- 6- and 8-bit RTN variants
+
+@pytest.mark.parametrize("bits,codes", [(8, [127, -64, 32, 13]), (6, [31, -16, 8, 3]), (4, [7, -4, 2, 1])])
+def test_rtn_bits_worked_example(bits, codes):
+    """y = (1, -0.5, 0.25, 0.1): s = 1/qmax, y/s = qmax * y.  8 bits: 127,
+    -63.5 (a tie, to even: -64), 31.75, 12.7.  6 bits: 31, -15.5 (-16), 7.75,
+    3.1.  4 bits: 7, -3.5 (-4), 1.75, 0.7."""
+    qmax = 2 ** (bits - 1) - 1
+    q, s, t = O.quantize_symmetric(np.array([[1.0, -0.5, 0.25, 0.1]]), bits=bits)
+    assert q[0].tolist() == codes
+    assert s[0] == pytest.approx(1.0 / qmax, rel=1e-15)
+
+
+@pytest.mark.parametrize("bits", [6, 8])
+@pytest.mark.parametrize("group", [0, 128])
+def test_rtn_bits_invariants(bits, group):
+    qmax = 2 ** (bits - 1) - 1
+    y = np.random.default_rng(9).laplace(size=(32, 512)) * np.where(np.arange(512) % 89 == 0, 40, 1)
+    q, s, t = O.quantize_symmetric(y, group, bits)
+    assert q.min() >= -qmax and q.max() <= qmax
+    g = 512 if group == 0 else group
+    assert np.all(np.abs(q.reshape(32, -1, g)).max(axis=2) == qmax)
+    deq = O.dequantize_symmetric(q, s, group)
+    sb = np.repeat(s.reshape(32, -1), g, axis=1)
+    assert np.all(np.abs(y - deq) <= sb / 2 * (1 + 1e-12))
+
+
+def test_rtn_bits_one_hot_closed_form():
+    """x = c e_k under D H / sqrt(n): every |y_i| = |c| / sqrt(n), so every code
+    is +-qmax with the sign of d_k H[k, i] c."""
+    n, k, c = 512, 37, -3.0
+    d = np.where(np.random.default_rng(4).random(n) < 0.5, -1, 1)
+    x = np.zeros((1, n))
+    x[0, k] = c
+    y = O.rotate(x, O.rotation_matrix(n, signs=d))
+    for bits in (6, 8):
+        qmax = 2 ** (bits - 1) - 1
+        q, s, _ = O.quantize_symmetric(y, bits=bits)
+        expect = qmax * np.sign(c) * d[k] * np.array([O.hadamard_entry(k, i) for i in range(n)])
+        assert np.array_equal(q[0], expect.astype(np.int8))
+        assert s[0] == pytest.approx(abs(c) / np.sqrt(n) / qmax, rel=1e-12)
+
+
+def test_rtn_6_8_bits_near_lossless():
+    """QuaRot abstract: plain RTN at 6 and 8 bits is (near) lossless.  On the
+    c1 layer with planted outliers the rotated output error falls about 4x
+    per two bits: ~16% (4 bits), ~3.6% (6), ~0.9% (8), and rotation still
+    beats no rotation at every width."""
+    c = W.CONFIGS["c1"]
+    x, w = W.make_x(c), W.make_w(c)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    r = O.rotation_matrix(c.K, signs=W.make_signs(c))
+    err = {b: _rel_err(O.linear_w4a4(x, w, r, bits=b)["out"], ref) for b in (4, 6, 8)}
+    plain = {b: _rel_err(O.linear_w4a4(x, w, np.eye(c.K), bits=b)["out"], ref) for b in (4, 6, 8)}
+    assert err[8] < 0.015 and err[6] < 0.05 and err[4] > 0.1
+    assert 2.5 < err[4] / err[6] < 6 and 2.5 < err[6] / err[8] < 6
+    assert all(err[b] < plain[b] for b in (4, 6, 8))
