@@ -119,8 +119,8 @@ qr_status qr_rotate_quant(const void *x_f16, int64_t rows, int64_t ld_x,
  * a_scales  device, fp32 [M] or [M][K/group]
  * w_codes   device, [N][K/2] packed codes, one row per output channel
  * w_scales  device, fp32 [N] or [N][K/group]
- * M, N >= 0; K > 0 and a multiple of 128; group 0 or a multiple of 128 that
- * divides K.
+ * M, N >= 0; K > 0, a multiple of 128 and at most 131072 (the int32 sums
+ * stay exact); group 0 or a multiple of 128 that divides K.
  * y_f16     device, fp16 [M][ld_y], ld_y >= N, 2-byte aligned.
  *
  * M <= 64 runs the memory-bound decode kernel (weights streamed once); larger
@@ -128,6 +128,31 @@ qr_status qr_rotate_quant(const void *x_f16, int64_t rows, int64_t ld_x,
  */
 qr_status qr_int4_gemm(const uint8_t *a_codes, const float *a_scales,
                        const uint8_t *w_codes, const float *w_scales,
+                       int64_t M, int64_t N, int64_t K, int64_t group,
+                       void *y_f16, int64_t ld_y, void *stream);
+
+/*
+ * 6- and 8-bit variants (QuaRot abstract: plain round-to-nearest gives
+ * lossless 6- and 8-bit models).  The same rotation and symmetric RTN with
+ * qmax = 2^(bits-1) - 1 (31 or 127) in place of 7:
+ *   s = max |y| / qmax,  q = clamp(rint(y / s), -qmax-1, qmax)
+ * codes are int8, one per byte, [rows][n] (16-byte aligned), not packed.
+ * bits is 6 or 8 (anything else: QR_EINVAL); all other arguments as for
+ * qr_rotate_quant.  Widths 4096 and 8192 without a dense factor (group 0 or
+ * 128) run the MFMA kernel; other rotations run the reference-shape kernel.
+ */
+qr_status qr_rotate_quant_i8(const void *x_f16, int64_t rows, int64_t ld_x,
+                             const qr_rotation *rot, int64_t group, int64_t bits,
+                             int8_t *codes, float *scales, void *stream);
+
+/*
+ * The GEMM of qr_int4_gemm on int8 codes (the 6- and 8-bit variants): the
+ * codes go into the int8 matrix cores as they are.  a_codes [M][K] and
+ * w_codes [N][K] int8 (16-byte aligned); every other argument and the
+ * epilogue as for qr_int4_gemm.  K <= 131072 keeps the int32 sums exact.
+ */
+qr_status qr_int8_gemm(const int8_t *a_codes, const float *a_scales,
+                       const int8_t *w_codes, const float *w_scales,
                        int64_t M, int64_t N, int64_t K, int64_t group,
                        void *y_f16, int64_t ld_y, void *stream);
 
@@ -212,6 +237,11 @@ qr_status qr_kv_attn_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_
  * qr_int4_gemm.
  */
 qr_status qr_int4_gemm_i32(const uint8_t *a_codes, const uint8_t *w_codes,
+                           int64_t M, int64_t N, int64_t K, int64_t group,
+                           int32_t *acc, void *stream);
+
+/* The same test export for qr_int8_gemm (int8 codes [M][K], [N][K]). */
+qr_status qr_int8_gemm_i32(const int8_t *a_codes, const int8_t *w_codes,
                            int64_t M, int64_t N, int64_t K, int64_t group,
                            int32_t *acc, void *stream);
 

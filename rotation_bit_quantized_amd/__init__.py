@@ -21,8 +21,8 @@ import torch
 
 __all__ = [
     "QRError", "LibraryNotBuilt", "Rotation", "library", "library_path", "rotate_quant", "int4_gemm",
-    "int4_gemm_i32", "kv_quant", "kv_attn_decode", "kv_attn_decode_workspace", "status_str", "version",
-    "EXPORTS",
+    "int4_gemm_i32", "kv_quant", "kv_attn_decode", "kv_attn_decode_workspace", "rotate_quant_i8",
+    "int8_gemm", "int8_gemm_i32", "status_str", "version", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +31,8 @@ _lib = None
 
 QR_OK, QR_EINVAL, QR_ESHAPE, QR_EALIGN, QR_EDEVICE = 0, 1, 2, 3, 4
 EXPORTS = ("qr_rotate_quant", "qr_int4_gemm", "qr_kv_quant", "qr_int4_gemm_i32", "qr_kv_attn_decode",
-           "qr_kv_attn_decode_workspace", "qr_status_str", "qr_version")
+           "qr_kv_attn_decode_workspace", "qr_rotate_quant_i8", "qr_int8_gemm", "qr_int8_gemm_i32",
+           "qr_status_str", "qr_version")
 
 
 class QRError(RuntimeError):
@@ -75,6 +76,12 @@ def library():
     lib.qr_kv_attn_decode.restype = st
     lib.qr_kv_attn_decode_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.qr_kv_attn_decode_workspace.restype = st
+    lib.qr_rotate_quant_i8.argtypes = [vp, i64, i64, ctypes.POINTER(_Rot), i64, i64, vp, vp, vp]
+    lib.qr_rotate_quant_i8.restype = st
+    lib.qr_int8_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i64, vp]
+    lib.qr_int8_gemm.restype = st
+    lib.qr_int8_gemm_i32.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp]
+    lib.qr_int8_gemm_i32.restype = st
     lib.qr_status_str.argtypes = [st]
     lib.qr_status_str.restype = ctypes.c_char_p
     lib.qr_version.argtypes = []
@@ -283,3 +290,62 @@ def kv_attn_decode(q, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros, le
                                      float(sm_scale), _ptr(ws), ws_bytes, _ptr(out), _stream(stream))
     _check("qr_kv_attn_decode", st)
     return out
+
+
+def rotate_quant_i8(x: torch.Tensor, rot: Rotation, bits: int, group: int = 0, codes=None, scales=None,
+                    stream=None):
+    """qr_rotate_quant_i8 (6- or 8-bit RTN) on the rows of x (fp16 [rows, >= n],
+    unit column stride).  Returns (codes int8 [rows, n], scales fp32 [rows] or
+    [rows, n/group])."""
+    _need(x, torch.float16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows = x.shape[0]
+    if codes is None:
+        codes = torch.empty((rows, rot.n), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows,) if group == 0 else (rows, rot.n // group), dtype=torch.float32,
+                             device=x.device)
+    _need(codes, torch.int8, "codes")
+    _need(scales, torch.float32, "scales")
+    ld = x.stride(0) if rows > 1 else max(x.stride(0), rot.n + (-rot.n) % 8)
+    st = library().qr_rotate_quant_i8(_ptr(x), rows, ld, ctypes.byref(rot._c), int(group), int(bits),
+                                      _ptr(codes), _ptr(scales), _stream(stream))
+    _check("qr_rotate_quant_i8", st)
+    return codes, scales
+
+
+def int8_gemm(a_codes, a_scales, w_codes, w_scales, group: int = 0, y=None, stream=None):
+    """qr_int8_gemm: a_codes int8 [M, K], w_codes int8 [N, K] -> y fp16 [M, N]."""
+    for t, dt, nm in ((a_codes, torch.int8, "a_codes"), (w_codes, torch.int8, "w_codes"),
+                      (a_scales, torch.float32, "a_scales"), (w_scales, torch.float32, "w_scales")):
+        _need(t, dt, nm)
+    M, K = a_codes.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] != K:
+        raise ValueError("K mismatch between a_codes and w_codes")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=a_codes.device)
+    _need(y, torch.float16, "y")
+    ld = y.stride(0) if M > 1 else max(y.stride(0), N)
+    st = library().qr_int8_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), M, N, K,
+                                int(group), _ptr(y), ld, _stream(stream))
+    _check("qr_int8_gemm", st)
+    return y
+
+
+def int8_gemm_i32(a_codes, w_codes, group: int = 0, acc=None, stream=None):
+    """qr_int8_gemm_i32: exact integer sums of int8 codes, int32 [M, N] or
+    [K/group, M, N]."""
+    _need(a_codes, torch.int8, "a_codes")
+    _need(w_codes, torch.int8, "w_codes")
+    M, K = a_codes.shape
+    N = w_codes.shape[0]
+    if acc is None:
+        shape = (M, N) if group == 0 else (K // group, M, N)
+        acc = torch.empty(shape, dtype=torch.int32, device=a_codes.device)
+    _need(acc, torch.int32, "acc")
+    st = library().qr_int8_gemm_i32(_ptr(a_codes), _ptr(w_codes), M, N, K, int(group), _ptr(acc),
+                                    _stream(stream))
+    _check("qr_int8_gemm_i32", st)
+    return acc

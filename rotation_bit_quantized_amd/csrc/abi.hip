@@ -27,7 +27,9 @@ qr_status check_rotation(const qr_rotation *rot) {
 
 qr_status check_gemm(const uint8_t *a, const uint8_t *w, int64_t M, int64_t N, int64_t K, int64_t group) {
   if (M < 0 || N < 0 || K <= 0) return QR_EINVAL;
-  if (K % 128 != 0 || K > (int64_t)1 << 20) return QR_ESHAPE;
+  // |product| <= 128 * 128 (8-bit codes, or 4-bit codes widened to 16 q):
+  // int32 sums stay exact for K <= 2^17
+  if (K % 128 != 0 || K > (int64_t)1 << 17) return QR_ESHAPE;
   if (group != 0 && (group < 128 || group % 128 != 0 || K % group != 0)) return QR_ESHAPE;
   if (M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30)) return QR_ESHAPE;
   if (M == 0 || N == 0) return QR_OK;
@@ -75,6 +77,60 @@ qr_status qr_rotate_quant(const void *x_f16, int64_t rows, int64_t ld_x, const q
   if (qr::rq_kron4096_supported(r, (int)group))
     return from_hip(qr::launch_rq_kron4096(x_f16, rows, ld_x, r, codes, scales, s));
   return from_hip(qr::launch_rq_generic(x_f16, rows, ld_x, r, (int)group, codes, scales, s));
+}
+
+qr_status qr_rotate_quant_i8(const void *x_f16, int64_t rows, int64_t ld_x, const qr_rotation *rot,
+                             int64_t group, int64_t bits, int8_t *codes, float *scales, void *stream) {
+  qr_status st = check_rotation(rot);
+  if (st != QR_OK) return st;
+  if (bits != 6 && bits != 8) return QR_EINVAL;
+  if (rows < 0) return QR_EINVAL;
+  if (group != 0 && (group < 32 || !pow2(group) || rot->n % group != 0)) return QR_ESHAPE;
+  if (ld_x < rot->n) return QR_ESHAPE;
+  if (ld_x % 8 != 0) return QR_EALIGN;
+  if (rows == 0) return QR_OK;
+  if (x_f16 == nullptr || codes == nullptr || scales == nullptr) return QR_EINVAL;
+  if (!aligned(x_f16, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return QR_EALIGN;
+  if (rot->signs != nullptr && !aligned(rot->signs, 4)) return QR_EALIGN;
+
+  qr::RotArgs r{(int)rot->n, (int)rot->had_n, (int)rot->dense_m, rot->dense, rot->signs};
+  hipStream_t s = (hipStream_t)stream;
+  if (qr::rq_pow2_supported(r, (int)group))
+    return from_hip(qr::launch_rq_pow2_bits(x_f16, rows, ld_x, r, (int)group, (int)bits, (uint8_t *)codes, scales, s));
+  return from_hip(
+      qr::launch_rq_generic_bits(x_f16, rows, ld_x, r, (int)group, (int)bits, (uint8_t *)codes, scales, s));
+}
+
+qr_status qr_int8_gemm(const int8_t *a_codes, const float *a_scales, const int8_t *w_codes,
+                       const float *w_scales, int64_t M, int64_t N, int64_t K, int64_t group, void *y_f16,
+                       int64_t ld_y, void *stream) {
+  qr_status st = check_gemm((const uint8_t *)a_codes, (const uint8_t *)w_codes, M, N, K, group);
+  if (st != QR_OK) return st;
+  if (ld_y < N) return QR_ESHAPE;
+  if (M == 0 || N == 0) return QR_OK;
+  if (a_scales == nullptr || w_scales == nullptr || y_f16 == nullptr) return QR_EINVAL;
+  if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(y_f16, 2)) return QR_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (M <= 64)
+    return from_hip(qr::launch_gemm_decode_i8(a_codes, a_scales, w_codes, w_scales, M, N, K, (int)group, y_f16,
+                                              ld_y, false, s));
+  return from_hip(qr::launch_gemm_prefill_i8(a_codes, a_scales, w_codes, w_scales, M, N, K, (int)group, y_f16,
+                                             ld_y, false, s));
+}
+
+qr_status qr_int8_gemm_i32(const int8_t *a_codes, const int8_t *w_codes, int64_t M, int64_t N, int64_t K,
+                           int64_t group, int32_t *acc, void *stream) {
+  qr_status st = check_gemm((const uint8_t *)a_codes, (const uint8_t *)w_codes, M, N, K, group);
+  if (st != QR_OK) return st;
+  if (M == 0 || N == 0) return QR_OK;
+  if (acc == nullptr) return QR_EINVAL;
+  if (!aligned(acc, 4)) return QR_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (M <= 64)
+    return from_hip(qr::launch_gemm_decode_i8(a_codes, nullptr, w_codes, nullptr, M, N, K, (int)group, acc, N,
+                                              true, s));
+  return from_hip(qr::launch_gemm_prefill_i8(a_codes, nullptr, w_codes, nullptr, M, N, K, (int)group, acc, N,
+                                             true, s));
 }
 
 qr_status qr_int4_gemm(const uint8_t *a_codes, const float *a_scales, const uint8_t *w_codes,

@@ -15,6 +15,10 @@
 // v_mfma_i32_16x16x64_i8 with A = weight rows, B = token rows, giving
 // C[channel][token].  The 16 per-wave partials are reduced through LDS in
 // int32 (per-channel, exact) or fp32 (group-wise, after scaling).
+//
+// 8-bit codes (CB = 8; the 6- and 8-bit RTN variants, QuaRot abstract): a
+// lane's 16 codes of a 64-code step are 16 bytes, used as the MFMA operand
+// as they are (no widening, no 1/256).
 #include "qr_common.h"
 #include "qr_launch.h"
 
@@ -33,7 +37,7 @@ __device__ __forceinline__ v4i widen8(v2u w) {
   return op;
 }
 
-template <bool GROUPED, bool OUT_I32>
+template <bool GROUPED, bool OUT_I32, int CB = 4>
 __global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ W,
     const float *__restrict__ sw, int M, int N, int K, int group, void *__restrict__ out, int64_t ld_y) {
@@ -44,13 +48,17 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n0 = blockIdx.x * kNT;
-  const int64_t kbytes = K / 2;
+  static_assert(CB == 4 || CB == 8, "code width");
+  constexpr int SHIFT = CB == 4 ? 8 : 0;           // widened 4-bit products carry 16 * 16
+  constexpr float UNSCALE = CB == 4 ? 1.0f / 256.0f : 1.0f;
+  constexpr int STEP_BYTES = 64 * CB / 8;          // bytes of a 64-code step per row
+  const int64_t kbytes = (int64_t)K * CB / 8;
   const int ksteps_per_unit = GROUPED ? group / 64 : 1;
   const int units = K / 64 / ksteps_per_unit;
   const int G = GROUPED ? K / group : 1;
 
   const int wrow = n0 + (lane & 15);                 // weight row (output channel) of this lane
-  const int kofs = (lane >> 4) * 8;                  // byte offset of this lane's 16 codes in a 64-code step
+  const int kofs = (lane >> 4) * (STEP_BYTES / 4);   // byte offset of this lane's 16 codes in a 64-code step
   const bool wvalid = wrow < N;
   const uint8_t *wp = W + (int64_t)(wvalid ? wrow : 0) * kbytes + kofs;
   const uint8_t *ap[4];
@@ -68,18 +76,24 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
   for (int u = wave; u < units; u += kWaves) {
     v4i uacc[4] = {v4i{}, v4i{}, v4i{}, v4i{}};
     for (int s = 0; s < ksteps_per_unit; ++s) {
-      const int64_t off = (int64_t)(u * ksteps_per_unit + s) * 32;
-      v2u wv = wvalid ? __builtin_nontemporal_load((const v2u *)(wp + off)) : v2u{0u, 0u};
-      v2u av[4];
+      const int64_t off = (int64_t)(u * ksteps_per_unit + s) * STEP_BYTES;
+      v4i wop, aop[4];
+      if constexpr (CB == 4) {
+        v2u wv = wvalid ? __builtin_nontemporal_load((const v2u *)(wp + off)) : v2u{0u, 0u};
+        wop = widen8(wv);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) av[f] = avalid[f] ? *(const v2u *)(ap[f] + off) : v2u{0u, 0u};
-      const v4i wop = widen8(wv);
+        for (int f = 0; f < 4; ++f) aop[f] = widen8(avalid[f] ? *(const v2u *)(ap[f] + off) : v2u{0u, 0u});
+      } else {
+        wop = wvalid ? __builtin_nontemporal_load((const v4i *)(wp + off)) : v4i{};
+#pragma unroll
+        for (int f = 0; f < 4; ++f) aop[f] = avalid[f] ? *(const v4i *)(ap[f] + off) : v4i{};
+      }
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         if (GROUPED)
-          uacc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, widen8(av[f]), uacc[f], 0, 0, 0);
+          uacc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop[f], uacc[f], 0, 0, 0);
         else
-          acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, widen8(av[f]), acc[f], 0, 0, 0);
+          acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop[f], acc[f], 0, 0, 0);
       }
     }
     if constexpr (GROUPED) {
@@ -92,14 +106,14 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int ch = n0 + 4 * (lane >> 4) + r;
-            if (t < M && ch < N) o[(int64_t)t * N + ch] = uacc[f][r] >> 8;
+            if (t < M && ch < N) o[(int64_t)t * N + ch] = uacc[f][r] >> SHIFT;
           }
         }
       } else {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const int t = f * 16 + (lane & 15);
-          const float sav = t < M ? sa[(int64_t)t * G + u] * (1.0f / 256.0f) : 0.f;
+          const float sav = t < M ? sa[(int64_t)t * G + u] * UNSCALE : 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int ch = n0 + 4 * (lane >> 4) + r;
@@ -136,12 +150,31 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) sum += red[w][f][l][r];
     if constexpr (OUT_I32) {
-      ((int32_t *)out)[(int64_t)t * N + ch] = sum >> 8;
+      ((int32_t *)out)[(int64_t)t * N + ch] = sum >> SHIFT;
     } else {
-      const float val = (float)sum * (sa[t] * sw[ch] * (1.0f / 256.0f));
+      const float val = (float)sum * (sa[t] * sw[ch] * UNSCALE);
       ((unsigned short *)out)[(int64_t)t * ld_y + ch] = float_to_half_bits(val);
     }
   }
+}
+
+template <int CB>
+hipError_t launch_decode(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw, int64_t M, int64_t N,
+                         int64_t K, int group, void *y, int64_t ld_y, bool out_i32, hipStream_t stream) {
+  dim3 grid((unsigned)((N + kNT - 1) / kNT)), block(64 * kWaves);
+  if (group == 0) {
+    if (out_i32)
+      gemm_decode_kernel<false, true, CB><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, 0, y, ld_y);
+    else
+      gemm_decode_kernel<false, false, CB><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, 0, y, ld_y);
+  } else {
+    if (out_i32)
+      gemm_decode_kernel<true, true, CB><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y);
+    else
+      gemm_decode_kernel<true, false, CB><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, group, y,
+                                                                      ld_y);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -149,19 +182,14 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
 hipError_t launch_gemm_decode(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,
                               int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
                               bool out_i32, hipStream_t stream) {
-  dim3 grid((unsigned)((N + kNT - 1) / kNT)), block(64 * kWaves);
-  if (group == 0) {
-    if (out_i32)
-      gemm_decode_kernel<false, true><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, 0, y, ld_y);
-    else
-      gemm_decode_kernel<false, false><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, 0, y, ld_y);
-  } else {
-    if (out_i32)
-      gemm_decode_kernel<true, true><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y);
-    else
-      gemm_decode_kernel<true, false><<<grid, block, 0, stream>>>(a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y);
-  }
-  return hipGetLastError();
+  return launch_decode<4>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+}
+
+hipError_t launch_gemm_decode_i8(const int8_t *a, const float *sa, const int8_t *w, const float *sw,
+                                 int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
+                                 bool out_i32, hipStream_t stream) {
+  return launch_decode<8>((const uint8_t *)a, sa, (const uint8_t *)w, sw, M, N, K, group, y, ld_y, out_i32,
+                          stream);
 }
 
 }  // namespace qr

@@ -1,4 +1,5 @@
-// 4-bit integer GEMM for prefill shapes (M > 64): y = dequant(qa . qw^T).
+// 4-bit (and 8-bit) integer GEMM for prefill shapes (M > 64):
+// y = dequant(qa . qw^T).
 //
 // Method: QuaRot abstract (all matrix multiplications in 4 bits);
 // dequantizing epilogue y = acc * s_x * s_w per output channel, or the sum
@@ -37,6 +38,11 @@
 // Compute: each wave owns a WM x WN sub-tile of 32x32 fragments of
 // v_mfma_i32_32x32x32_i8, so each widened operand feeds FN (or FM) MFMAs.
 // The host picks the block shape whose tile count fills the CU slots best.
+//
+// 8-bit codes (the 6- and 8-bit RTN variants; QuaRot abstract: lossless 6-
+// and 8-bit RTN): the same kernel with CB = 8.  A K-tile is still 128 bytes
+// per row, now 128 codes; a 16-byte fragment read is one MFMA k-step used as
+// is (no widening, no 1/256).
 #include "qr_common.h"
 #include "qr_launch.h"
 
@@ -45,9 +51,7 @@
 namespace qr {
 namespace {
 
-constexpr int kBK = 256;         // codes per K-tile
-constexpr int kRowBytes = 128;   // bytes per row per K-tile
-constexpr int kHalfCodes = 128;  // a group spans whole halves of a K-tile
+constexpr int kRowBytes = 128;   // bytes per row per K-tile (256 4-bit or 128 8-bit codes)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -107,10 +111,17 @@ __device__ __forceinline__ void tile_of(int bid, int tm_count, int tn_count, int
 // OCC waves per SIMD: blocks of 4 waves run OCC to a CU, blocks of 8 waves
 // OCC/2.  At OCC 1 a wave has the whole register file (AGPR accumulators).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GROUPED, bool OUT_I32, bool SHORT_TAIL,
-          int OCC = 2>
+          int OCC = 2, int CB = 4>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_N)) void gemm_prefill_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ W,
     const float *__restrict__ sw, int M, int N, int K, int group, void *__restrict__ out, int64_t ld_y) {
+  static_assert(CB == 4 || CB == 8, "code width");
+  constexpr int kBK = CB == 4 ? 256 : 128;        // codes per K-tile
+  constexpr int kHalfCodes = kBK / 2;             // a group spans whole halves of a K-tile
+  constexpr int KS = CB == 4 ? 2 : 1;             // MFMA k-steps per 16-byte fragment read
+  constexpr int SHIFT = CB == 4 ? 8 : 0;          // widened 4-bit products carry 16 * 16
+  constexpr float UNSCALE = CB == 4 ? 1.0f / 256.0f : 1.0f;
+  static_assert(CB == 4 || !SHORT_TAIL, "8-bit K-tiles are whole");
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
@@ -149,7 +160,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   int tm, tn;
   tile_of(blockIdx.x, tm_count, tn_count, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int64_t kbytes = K / 2;
+  const int64_t kbytes = (int64_t)K * CB / 8;
   const int KT = (K + kBK - 1) / kBK;
   // SHORT_TAIL: K is an odd multiple of 128, the last K-tile holds 128 codes
   const int halves_per_group = GROUPED ? group / kHalfCodes : 1;
@@ -250,10 +261,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
     }
   };
   auto widen_into = [&](int rbuf, int obuf) __attribute__((always_inline)) {
+    if constexpr (CB == 4) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) widen(rawA[rbuf][i], opA[obuf][i][0], opA[obuf][i][1]);
+      for (int i = 0; i < FM; ++i) widen(rawA[rbuf][i], opA[obuf][i][0], opA[obuf][i][1]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) widen(rawB[rbuf][j], opB[obuf][j][0], opB[obuf][j][1]);
+      for (int j = 0; j < FN; ++j) widen(rawB[rbuf][j], opB[obuf][j][0], opB[obuf][j][1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) opA[obuf][i][0] = __builtin_bit_cast(v4i, rawA[rbuf][i]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) opB[obuf][j][0] = __builtin_bit_cast(v4i, rawB[rbuf][j]);
+    }
   };
   // The MFMAs of the chunk in operand buffer `obuf` (two k-steps); with
   // ZERO the first k-step starts from zero (a new K-group).  DMA
@@ -264,7 +282,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
     constexpr bool ZERO = decltype(zero_c)::value;
     constexpr int Q_LO = decltype(dma_c)::lo, Q_HI = decltype(dma_c)::hi;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -275,7 +293,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(opA[obuf][i][ks], opB[obuf][j][ks], acc[i][j], 0, 0, 0);
           // DMA instructions spaced evenly over the chunk's MFMAs: after
           // MFMA idx when idx is a multiple of the spacing
-          constexpr int NMF = 2 * FM * FN, ND = Q_HI - Q_LO;
+          constexpr int NMF = KS * FM * FN, ND = Q_HI - Q_LO;
           constexpr int SP = ND > 0 ? (NMF / ND > 0 ? NMF / ND : 1) : 1;
           const int idx = (ks * FM + i) * FN + j;
           if (idx % SP == 0 && idx / SP < ND) issue_q(dkt, dstage, Q_LO + idx / SP);
@@ -288,8 +306,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
                      int dstage) __attribute__((always_inline)) {
     constexpr bool DO_WIDEN = decltype(widen_c)::value;
     constexpr int ND = decltype(dma_c)::hi - decltype(dma_c)::lo;
-    constexpr int NMFMA = 2 * FM * FN;
-    constexpr int NVALU = DO_WIDEN ? 12 * (FM + FN) : 0;
+    constexpr int NMFMA = KS * FM * FN;
+    constexpr int NVALU = DO_WIDEN && CB == 4 ? 12 * (FM + FN) : 0;
     constexpr int VPM = (NVALU + NMFMA - 1) / NMFMA;
     if (GROUPED && zero) {
       mma_chunk(obuf, std::true_type{}, dma_c, dkt, dstage);
@@ -322,7 +340,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   auto read_scales = [&](int kt, int h) __attribute__((always_inline)) {
     const float *sc = (const float *)(scale_ring + (kt % 3) * SCALE_BYTES) + h * ROWS;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) gsw[j] = sc[BM + wn * WN + j * 32 + lcol] * (1.0f / 256.0f);
+    for (int j = 0; j < FN; ++j) gsw[j] = sc[BM + wn * WN + j * 32 + lcol] * UNSCALE;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -341,7 +359,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
-            if (row < M && col < N) o[(int64_t)row * N + col] = acc[i][j][r] >> 8;
+            if (row < M && col < N) o[(int64_t)row * N + col] = acc[i][j][r] >> SHIFT;
           }
         }
     } else {
@@ -382,7 +400,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   constexpr int kNext = 0, kNextNoDma = 1, kLastFull = 2, kLastShort = 3;
   constexpr int Q1 = LOADS / 2;
   static_assert(STAGES == 2, "the refill schedule assumes two stages");
-  static_assert(Q1 <= 2 * FM * FN && LOADS - Q1 <= 2 * FM * FN, "one DMA instruction per MFMA at most");
+  static_assert(Q1 <= KS * FM * FN && LOADS - Q1 <= KS * FM * FN, "one DMA instruction per MFMA at most");
   auto tile = [&](int kt, auto mode_c) __attribute__((always_inline)) {
     constexpr int mode = decltype(mode_c)::value;
     constexpr bool NEXT = mode == kNext || mode == kNextNoDma;
@@ -489,7 +507,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
-          if (row < M && col < N) o[(int64_t)row * N + col] = acc[i][j][r] >> 8;
+          if (row < M && col < N) o[(int64_t)row * N + col] = acc[i][j][r] >> SHIFT;
         }
       }
   } else if constexpr (!OUT_I32) {
@@ -508,7 +526,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
     float swv[FN], sav[GROUPED ? 1 : FM][16];
     if constexpr (!GROUPED) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) swv[j] = sw[min(n0 + wn * WN + j * 32 + lcol, N - 1)] * (1.0f / 256.0f);
+      for (int j = 0; j < FN; ++j) swv[j] = sw[min(n0 + wn * WN + j * 32 + lcol, N - 1)] * UNSCALE;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -564,34 +582,38 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GROUPED, int OCC = 2>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GROUPED, int CB, int OCC = 2>
 hipError_t launch_cfg(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw, int64_t M,
                       int64_t N, int64_t K, int group, void *y, int64_t ld_y, bool out_i32,
                       hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
-  const bool short_tail = K % kBK != 0;
 #define QR_GEMM_LAUNCH(I32, TAIL)                                                                \
-  gemm_prefill_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, GROUPED, I32, TAIL, OCC><<<grid, block, 0, stream>>>( \
+  gemm_prefill_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, GROUPED, I32, TAIL, OCC, CB><<<grid, block, 0, stream>>>( \
       a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y)
-  if (out_i32) {
-    if (short_tail) QR_GEMM_LAUNCH(true, true);
-    else QR_GEMM_LAUNCH(true, false);
-  } else {
-    if (short_tail) QR_GEMM_LAUNCH(false, true);
+  if constexpr (CB == 4) {
+    const bool short_tail = K % 256 != 0;
+    if (out_i32) {
+      if (short_tail) QR_GEMM_LAUNCH(true, true);
+      else QR_GEMM_LAUNCH(true, false);
+    } else {
+      if (short_tail) QR_GEMM_LAUNCH(false, true);
+      else QR_GEMM_LAUNCH(false, false);
+    }
+  } else {   // K % 128 == 0: whole 128-code tiles
+    if (out_i32) QR_GEMM_LAUNCH(true, false);
     else QR_GEMM_LAUNCH(false, false);
   }
 #undef QR_GEMM_LAUNCH
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemm_prefill(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,
-                               int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
-                               bool out_i32, hipStream_t stream) {
+template <int CB>
+hipError_t launch_prefill(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw, int64_t M,
+                          int64_t N, int64_t K, int group, void *y, int64_t ld_y, bool out_i32,
+                          hipStream_t stream) {
   if (group != 0)
-    return launch_cfg<128, 128, 2, 2, 2, true>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+    return launch_cfg<128, 128, 2, 2, 2, true, CB>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -609,10 +631,25 @@ hipError_t launch_gemm_prefill(const uint8_t *a, const float *sa, const uint8_t 
   const double s_256x192 = score(256, 192, 1, 1.0), s_128x192 = score(128, 192, 2, 0.95),
                s_128x128 = score(128, 128, 2, 0.93);
   if (s_256x192 >= s_128x192 && s_256x192 >= s_128x128)
-    return launch_cfg<256, 192, 4, 2, 2, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+    return launch_cfg<256, 192, 4, 2, 2, false, CB>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
   if (s_128x192 >= s_128x128)
-    return launch_cfg<128, 192, 2, 2, 2, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
-  return launch_cfg<128, 128, 2, 2, 2, false>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+    return launch_cfg<128, 192, 2, 2, 2, false, CB>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+  return launch_cfg<128, 128, 2, 2, 2, false, CB>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_prefill(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,
+                               int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
+                               bool out_i32, hipStream_t stream) {
+  return launch_prefill<4>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
+}
+
+hipError_t launch_gemm_prefill_i8(const int8_t *a, const float *sa, const int8_t *w, const float *sw,
+                                  int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
+                                  bool out_i32, hipStream_t stream) {
+  return launch_prefill<8>((const uint8_t *)a, sa, (const uint8_t *)w, sw, M, N, K, group, y, ld_y, out_i32,
+                           stream);
 }
 
 }  // namespace qr

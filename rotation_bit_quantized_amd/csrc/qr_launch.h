@@ -19,12 +19,17 @@ struct RotArgs {
 // Rotate + quantize, any validated shape (LDS-resident row, one block per row).
 hipError_t launch_rq_generic(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
                              uint8_t *codes, float *scales, hipStream_t stream);
+// bits 4 (packed) or 6, 8 (int8 codes, one per byte)
+hipError_t launch_rq_generic_bits(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group, int bits,
+                                  uint8_t *codes, float *scales, hipStream_t stream);
 
 // Rotate + quantize for n in {4096, 8192}, no dense factor, group 0 or 128
 // (first Hadamard factor on fp16 MFMA, the rest in registers, one wave per row).
 bool rq_pow2_supported(const RotArgs &r, int group);
 hipError_t launch_rq_pow2(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
                           uint8_t *codes, float *scales, hipStream_t stream);
+hipError_t launch_rq_pow2_bits(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group, int bits,
+                               uint8_t *codes, float *scales, hipStream_t stream);
 
 // Rotate + quantize for n = 64 * m with a dense m x m factor (m <= 176),
 // dense factor on fp16 MFMA (hi/lo split), 64-point Hadamard in registers.
@@ -45,6 +50,13 @@ hipError_t launch_gemm_prefill(const uint8_t *a, const float *sa, const uint8_t 
 hipError_t launch_gemm_decode(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,
                               int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
                               bool out_i32, hipStream_t stream);
+// The same GEMMs on int8 codes [rows][K] (the 6- and 8-bit variants).
+hipError_t launch_gemm_prefill_i8(const int8_t *a, const float *sa, const int8_t *w, const float *sw,
+                                  int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
+                                  bool out_i32, hipStream_t stream);
+hipError_t launch_gemm_decode_i8(const int8_t *a, const float *sa, const int8_t *w, const float *sw,
+                                 int64_t M, int64_t N, int64_t K, int group, void *y, int64_t ld_y,
+                                 bool out_i32, hipStream_t stream);
 
 // Decode attention over the rotated 4-bit KV cache, head_dim 128.  The plan
 // (tokens per chunk, chunks per sequence, workspace size) depends on the

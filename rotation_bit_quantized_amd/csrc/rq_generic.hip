@@ -5,8 +5,10 @@
 //   1. x * signs                       (the random diagonal D, input side)
 //   2. dense factor: t[i*m + b] = sum_a x[i*m + a] O[a][b]   (if m > 1)
 //   3. Walsh-Hadamard butterflies over the Hadamard index i, in place
-//   4. max |.| per row or per group, s = max / (7 sqrt(p)), codes
-//      rint(v * 7 / max), packed two per byte.
+//   4. max |.| per row or per group, s = max / (qmax sqrt(p)), codes
+//      rint(v * qmax / max): qmax = 7 packed two per byte, or the 6- and
+//      8-bit variants qmax = 31, 127 as one int8 per byte (QuaRot abstract:
+//      lossless 6- and 8-bit RTN).
 // This is the reference-shape path of the library: small or unusual widths
 // (n = 2 .. 32768, any power-of-two Hadamard size, dense factors up to 256;
 // a factor of size m <= 16 is applied in place, one i-group per thread in
@@ -27,7 +29,7 @@ constexpr int kInPlaceM = 16;   // dense factors up to this size are applied in 
 
 __global__ __launch_bounds__(kBlock) void rq_generic_kernel(
     const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, int n, int had_n, int dense_m,
-    const float *__restrict__ dense, const int8_t *__restrict__ signs, int group,
+    const float *__restrict__ dense, const int8_t *__restrict__ signs, int group, int qmax,
     uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
   extern __shared__ float smem[];
   float *buf = smem;
@@ -107,8 +109,17 @@ __global__ __launch_bounds__(kBlock) void rq_generic_kernel(
     }
     __syncthreads();
 
+    if (qmax > 7) {
+      int8_t *cr8 = (int8_t *)codes + row * (int64_t)n;
+      const float qm = (float)qmax;
+      for (int k = tid; k < n; k += kBlock) {
+        const float m = red[k / g];
+        const int q = (int)rintf(cur[k] * (m > 0.f ? qm / m : 0.f));
+        cr8[k] = (int8_t)min(qmax, max(-qmax - 1, q));
+      }
+    }
     uint8_t *cr = codes + row * (int64_t)(n / 2);
-    for (int c = tid; c < n / 2; c += kBlock) {
+    for (int c = tid; c < (qmax > 7 ? 0 : n / 2); c += kBlock) {
       const int k = 2 * c;
       const float m0 = red[k / g];
       const float m1 = red[(k + 1) / g];
@@ -129,6 +140,12 @@ __global__ __launch_bounds__(kBlock) void rq_generic_kernel(
 
 hipError_t launch_rq_generic(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
                              uint8_t *codes, float *scales, hipStream_t stream) {
+  return launch_rq_generic_bits(x, rows, ld_x, r, group, 4, codes, scales, stream);
+}
+
+hipError_t launch_rq_generic_bits(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group, int bits,
+                                  uint8_t *codes, float *scales, hipStream_t stream) {
+  const int qmax = (1 << (bits - 1)) - 1;
   const int g = group ? group : r.n;
   const bool two_copies = r.dense_m > kInPlaceM;
   const size_t lds = sizeof(float) * ((two_copies ? 2 * (size_t)r.n : (size_t)r.n) + (size_t)(r.n / g));
@@ -138,9 +155,9 @@ hipError_t launch_rq_generic(const void *x, int64_t rows, int64_t ld_x, const Ro
     if (e != hipSuccess) return e;
   }
   const int64_t grid = rows < 4096 ? rows : 4096;
-  const float scale_mul = (float)(1.0 / (7.0 * __builtin_sqrt((double)r.had_n)));
+  const float scale_mul = (float)(1.0 / ((double)qmax * __builtin_sqrt((double)r.had_n)));
   rq_generic_kernel<<<dim3((unsigned)grid), dim3(kBlock), lds, stream>>>(
-      (const unsigned short *)x, rows, ld_x, r.n, r.had_n, r.dense_m, r.dense, r.signs, group, codes,
+      (const unsigned short *)x, rows, ld_x, r.n, r.had_n, r.dense_m, r.dense, r.signs, group, qmax, codes,
       scales, scale_mul);
   return hipGetLastError();
 }

@@ -30,6 +30,9 @@
 //    n = 8192) and lane l owns outputs [64 l, 64 l + 64): absmax, rounding
 //    and packing stay in the lane and the codes go out as 16-byte stores.
 // The 1/sqrt(n) is folded into the stored scale (codes do not depend on it).
+// BITS = 6 or 8 (QuaRot abstract: lossless 6- and 8-bit RTN): s = max|y|/qmax
+// with qmax = 2^(BITS-1) - 1, one int8 code per byte, four 16-byte stores
+// per lane and run.
 #include "qr_common.h"
 #include "qr_launch.h"
 
@@ -98,7 +101,7 @@ __device__ constexpr BopTable kBop = make_bop_table();
 
 // Register index of a value: bits 0-1 = r (MFMA output row within the 4-row
 // group), bits 2-3 = N-tile, bits 4.. = M-tile.
-template <int L, int GROUP>
+template <int L, int GROUP, int BITS = 4>
 __global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
     const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, const int8_t *__restrict__ signs,
     uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
@@ -108,9 +111,13 @@ __global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
   constexpr int MT = 1 << (L - 10);   // M-tiles of 16 rows of the 64-column view
   constexpr int NV = MT * 16;         // values per lane
   constexpr int RUNS = NV / 64;
-  // vector-memory instructions per row after its compute: two 16-byte code
-  // stores per run, then the scale stores (one per run for groups)
-  constexpr int STORES = 2 * RUNS + (GROUP == 0 ? 1 : RUNS);
+  static_assert(BITS == 4 || BITS == 6 || BITS == 8, "code width");
+  constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
+  constexpr int CODE_BYTES = BITS == 4 ? n / 2 : n;   // per row
+  constexpr int CODE_STORES = BITS == 4 ? 2 : 4;      // 16-byte stores per lane and run
+  // vector-memory instructions per row after its compute: the code stores
+  // of every run, then the scale stores (one per run for groups)
+  constexpr int STORES = CODE_STORES * RUNS + (GROUP == 0 ? 1 : RUNS);
   static_assert(L == 12 || L == 13, "pass-2 layout written for n = 4096, 8192");
   static_assert(2 * STORES + DMA < 64, "vmcnt range");
 
@@ -267,10 +274,29 @@ __global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
       for (int run = 0; run < RUNS; ++run) amax[run] = fmaxf(amax[run], __shfl_xor(amax[run], 1, 64));
     }
 
-    uint8_t *cr = codes + row * (int64_t)(n / 2);
+    uint8_t *cr = codes + row * (int64_t)CODE_BYTES;
 #pragma unroll
     for (int run = 0; run < RUNS; ++run) {
-      const float inv = amax[run] > 0.f ? 7.0f / amax[run] : 0.f;
+      const float inv = amax[run] > 0.f ? QMAX / amax[run] : 0.f;
+      if constexpr (BITS != 4) {
+        // 64 int8 codes of this lane, in output order, as 16 words
+        unsigned words[16];
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+          unsigned wd = 0u;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int e = 4 * w + t;  // position within the 64-run
+            const int i = ((e >> 2) & 3) | ((e & 3) << 2) | (((e >> 4) & 3) << 4);
+            wd |= (round_bits(v[run * 64 + i], inv) & 0xFFu) << (8 * t);
+          }
+          words[w] = wd;
+        }
+        v4u *dst = (v4u *)(cr + run * 4096 + 64 * lane);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = v4u{words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]};
+        continue;
+      }
       unsigned words[8];
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
@@ -298,7 +324,7 @@ __global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
   wait_vm<0>();   // no DMA may still be writing this block's LDS when it exits
 }
 
-template <int L, int GROUP>
+template <int L, int GROUP, int BITS = 4>
 hipError_t launch_one(const void *x, int64_t rows, int64_t ld_x, const int8_t *signs, uint8_t *codes,
                       float *scales, hipStream_t stream) {
   int dev = 0;
@@ -309,7 +335,7 @@ hipError_t launch_one(const void *x, int64_t rows, int64_t ld_x, const int8_t *s
   static int per_cu = 0;
   if (per_cu == 0) {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rq_pow2_kernel<L, GROUP>, 64 * kWaves, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rq_pow2_kernel<L, GROUP, BITS>, 64 * kWaves, 0) != hipSuccess ||
         b < 1)
       b = 1;
     per_cu = b;
@@ -317,8 +343,9 @@ hipError_t launch_one(const void *x, int64_t rows, int64_t ld_x, const int8_t *s
   const int64_t blocks_needed = (rows + kWaves - 1) / kWaves;
   const int64_t cap = (int64_t)cus * per_cu;
   const int64_t grid = blocks_needed < cap ? blocks_needed : cap;
-  const float scale_mul = (float)(1.0 / (7.0 * __builtin_sqrt((double)(1 << L))));
-  rq_pow2_kernel<L, GROUP><<<dim3((unsigned)grid), dim3(64 * kWaves), 0, stream>>>(
+  const double qmax = (double)((1 << (BITS - 1)) - 1);
+  const float scale_mul = (float)(1.0 / (qmax * __builtin_sqrt((double)(1 << L))));
+  rq_pow2_kernel<L, GROUP, BITS><<<dim3((unsigned)grid), dim3(64 * kWaves), 0, stream>>>(
       (const unsigned short *)x, rows, ld_x, signs, codes, scales, scale_mul);
   return hipGetLastError();
 }
@@ -331,12 +358,23 @@ bool rq_pow2_supported(const RotArgs &r, int group) {
 
 hipError_t launch_rq_pow2(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
                           uint8_t *codes, float *scales, hipStream_t stream) {
+  return launch_rq_pow2_bits(x, rows, ld_x, r, group, 4, codes, scales, stream);
+}
+
+hipError_t launch_rq_pow2_bits(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group, int bits,
+                               uint8_t *codes, float *scales, hipStream_t stream) {
+#define QR_POW2(L, B)                                                                          \
+  return group ? launch_one<L, 128, B>(x, rows, ld_x, r.signs, codes, scales, stream)          \
+               : launch_one<L, 0, B>(x, rows, ld_x, r.signs, codes, scales, stream)
   if (r.n == 4096) {
-    return group ? launch_one<12, 128>(x, rows, ld_x, r.signs, codes, scales, stream)
-                 : launch_one<12, 0>(x, rows, ld_x, r.signs, codes, scales, stream);
+    if (bits == 8) QR_POW2(12, 8);
+    if (bits == 6) QR_POW2(12, 6);
+    QR_POW2(12, 4);
   }
-  return group ? launch_one<13, 128>(x, rows, ld_x, r.signs, codes, scales, stream)
-               : launch_one<13, 0>(x, rows, ld_x, r.signs, codes, scales, stream);
+  if (bits == 8) QR_POW2(13, 8);
+  if (bits == 6) QR_POW2(13, 6);
+  QR_POW2(13, 4);
+#undef QR_POW2
 }
 
 }  // namespace qr

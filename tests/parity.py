@@ -116,3 +116,17 @@ def check_attn(gpu_fp16: np.ndarray, ref: np.ndarray, what: str = "attention"):
     assert np.all(np.abs(g - ref) <= ATTN_ABS_FRAC * peak + 1e-30), \
         f"{what}: max element error {np.abs(g - ref).max():.3e}"
     return float(rel.max()) if rel.size else 0.0
+
+
+def check_symmetric_int8(gpu: np.ndarray, q_or: np.ndarray, t_or: np.ndarray, what: str = "int8 codes"):
+    """The 6- and 8-bit codes (int8, unpacked) under the same boundary rule
+    as check_symmetric_codes."""
+    g = np.asarray(gpu).astype(np.int8)
+    assert g.shape == q_or.shape, (g.shape, q_or.shape)
+    mism = g != q_or
+    bad = mism & ~near_half(t_or)
+    nm, nb = int(mism.sum()), int(bad.sum())
+    assert nb == 0, f"{what}: {nb} mismatches away from a rounding boundary"
+    assert nm <= max(1, MAX_MISMATCH_FRAC * g.size), f"{what}: {nm} boundary mismatches"
+    assert np.all(np.abs(g.astype(np.int64) - q_or) <= 1), f"{what}: a mismatch larger than one step"
+    return nm

@@ -198,3 +198,23 @@ def test_attn_workspace_size():
     out = ctypes.c_int64(0)
     assert qr.library().qr_kv_attn_decode_workspace(1, 32, 32, -1, 128, ctypes.byref(out)) == qr.QR_EINVAL
     assert qr.library().qr_kv_attn_decode_workspace(1, 32, 32, 1, 128, None) == qr.QR_EINVAL
+
+
+def test_i8_rejects():
+    lib = qr.library()
+    rot = qr._Rot(4096, 4096, 1, None, None)
+    args = lambda bits=8, codes=A16: (A16, 4, 4096, ctypes.byref(rot), 0, bits, codes, A16, None)
+    assert lib.qr_rotate_quant_i8(*args(bits=5)) == qr.QR_EINVAL
+    assert lib.qr_rotate_quant_i8(*args(bits=4)) == qr.QR_EINVAL
+    assert lib.qr_rotate_quant_i8(*args(codes=MIS)) == qr.QR_EALIGN
+    assert lib.qr_rotate_quant_i8(*args(codes=None)) == qr.QR_EINVAL
+    assert lib.qr_rotate_quant_i8(A16, 0, 4096, ctypes.byref(rot), 0, 8, None, None, None) == qr.QR_OK
+    gemm = lambda M=128, N=128, K=512, g=0, a=A16: lib.qr_int8_gemm(a, A16, A16, A16, M, N, K, g, A16, N, None)
+    assert gemm(K=500) == qr.QR_ESHAPE
+    assert gemm(K=(1 << 17) + 128) == qr.QR_ESHAPE        # int32 sums would not stay exact
+    assert gemm(g=64) == qr.QR_ESHAPE
+    assert gemm(a=MIS) == qr.QR_EALIGN
+    assert gemm(a=None) == qr.QR_EINVAL
+    assert gemm(M=0) == qr.QR_OK
+    assert lib.qr_int8_gemm_i32(A16, A16, 128, 128, 512, 0, None, None) == qr.QR_EINVAL
+    assert lib.qr_int8_gemm_i32(A16, A16, 128, 128, 512, 0, MIS, None) == qr.QR_EALIGN
