@@ -259,6 +259,35 @@ def suite(args):
              GBs=round(nbytes / ms / 1e6, 1), frac_hbm=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
              bytes=nbytes, weight_sets=stream_w)
 
+    def gemm8_case(name, M, N, K, group, reps=10):
+        if only and name not in only:
+            return
+        G = 1 if group == 0 else K // group
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+        w = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g)
+        sa = torch.rand((M,) if group == 0 else (M, G), device=dev, generator=g) * 0.001
+        sw = torch.rand((N,) if group == 0 else (N, G), device=dev, generator=g) * 0.001
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ms = time_launches(lambda i: qr.int8_gemm(a, sa, w, sw, group, y=y), reps)
+        ops = 2.0 * M * N * K
+        emit(name, kernel="qr_int8_gemm", shape=[M, N, K], group=group, us=round(ms * 1e3, 3),
+             TOPS=round(ops / ms / 1e9, 2), frac_int8=round(ops / ms / 1e9 / INT8_PEAK_TOPS, 4))
+
+    def rq8_case(name, cfg, rows, group, bits, reps=20):
+        if only and name not in only:
+            return
+        c = W.CONFIGS[cfg]
+        x = torch.from_numpy(W.make_x(c, rows=np.arange(rows))).to(dev)
+        rot = qr.Rotation.hadamard(c.K, W.make_signs(c))
+        nbytes = rows * c.K * 2 + rows * c.K + rows * 4 * (1 if group == 0 else c.K // group)
+        xs = copies(lambda: x.clone(), rows * c.K * 2)
+        outs = [qr.rotate_quant_i8(xx, rot, bits, group) for xx in xs]
+        ms = time_launches(lambda i: qr.rotate_quant_i8(xs[i % len(xs)], rot, bits, group, *outs[i % len(xs)]),
+                           reps)
+        emit(name, kernel="qr_rotate_quant_i8", shape=[rows, c.K], bits=bits, group=group, us=round(ms * 1e3, 3),
+             GBs=round(nbytes / ms / 1e6, 1), frac_hbm=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+             bytes=nbytes, buffers=len(xs))
+
     def kv_case(name, T, reps=20, cycle=True):
         if only and name not in only:
             return
@@ -308,6 +337,11 @@ def suite(args):
     gemm_case("gemm_c5_decode_streamed", 64, 4096, 4096, 0, reps=128, stream_w=64)
     kv_case("kv_c5_decode", 64, reps=50, cycle=False)
     kv_case("kv_prefill_131072", 131072, reps=5)
+    gemm8_case("gemm8_c2", 2048, 12288, 4096, 0)
+    gemm8_case("gemm8_c4_g128", 16384, 28672, 8192, 128, reps=3)
+    gemm8_case("gemm8_c5_decode", 64, 4096, 4096, 0, reps=50)
+    rq8_case("rq8_c2", "c2", 2048, 0, 8)
+    rq8_case("rq8_c4_g128", "c4", 16384, 128, 8)
     attn_case("attn_decode_b64_t2048", 64, 2048, 32, 32)
     attn_case("attn_decode_b1_t4096", 1, 4096, 32, 32, reps=50)
     attn_case("attn_decode_gqa_b64_t2048", 64, 2048, 64, 8)
