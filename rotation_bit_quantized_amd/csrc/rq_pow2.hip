@@ -59,15 +59,33 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Four waves per block, each with two row buffers: two of its rows stream in
-// while it works on a third.  n = 4096: 64 KB per block, two blocks per CU;
-// n = 8192: 128 KB, one block per CU.
-constexpr int kWaves = 4;
-constexpr int kBufs = 2;
-
+// n = 4096: four waves per block, each with two row buffers (two of its
+// rows stream in while it works on a third): 64 KB per block, two blocks per
+// CU.  n = 8192: eight waves per block, each with one row buffer refilled as
+// soon as pass 1 has read it (the row streams in while the wave transforms,
+// quantizes and stores the previous one), and the per-lane sign masks in
+// LDS rather than in 64 registers: 128 KB + 16 KB per block, one block per
+// CU, two waves per SIMD (the 1-wave-per-SIMD form left the SIMD idle on
+// its own latencies).
+template <int L>
+constexpr int waves_of() {
+  return L == 13 ? 8 : 4;
+}
+template <int L>
+constexpr int bufs_of() {
+  return L == 13 ? 1 : 2;
+}
+template <int L>
+constexpr bool lds_signs() {
+  return L == 13;
+}
+template <int L>
+constexpr int sign_lds_bytes() {
+  return lds_signs<L>() ? 64 * (8 << (L - 10)) * 4 : 0;   // [words / 4][lane][4] of unsigned
+}
 template <int L>
 constexpr int lds_bytes() {
-  return kWaves * kBufs * (2 << L);
+  return waves_of<L>() * bufs_of<L>() * (2 << L) + sign_lds_bytes<L>();
 }
 
 // The B operands (the +-1 64-point factor, columns permuted) of every lane,
@@ -102,7 +120,7 @@ __device__ constexpr BopTable kBop = make_bop_table();
 // Register index of a value: bits 0-1 = r (MFMA output row within the 4-row
 // group), bits 2-3 = N-tile, bits 4.. = M-tile.
 template <int L, int GROUP, int BITS = 4>
-__global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
+__global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
     const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, const int8_t *__restrict__ signs,
     uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
   constexpr int n = 1 << L;
@@ -120,11 +138,15 @@ __global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
   constexpr int STORES = CODE_STORES * RUNS + (GROUP == 0 ? 1 : RUNS);
   static_assert(L == 12 || L == 13, "pass-2 layout written for n = 4096, 8192");
   static_assert(2 * STORES + DMA < 64, "vmcnt range");
+  constexpr int kWaves = waves_of<L>();
+  constexpr int kBufs = bufs_of<L>();
+  constexpr bool SIGNS_LDS = lds_signs<L>();
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<L>()];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t *const bufs = smem + wave * kBufs * ROWB;
+  unsigned *const sign_lds = (unsigned *)(smem + kWaves * kBufs * ROWB);
 
   const int c16 = lane & 15;
   const int g = lane >> 4;
@@ -139,6 +161,45 @@ __global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
 
   const int64_t wave_id = (int64_t)blockIdx.x * kWaves + wave;
   const int64_t wave_stride = (int64_t)gridDim.x * kWaves;
+
+  // Sign masks for the pieces this lane reads: piece (m, s, h) covers
+  // elements base + 0..3 with base = 4 c16 + 64 g + 256 h + 512 s + 1024 m;
+  // their four int8 signs are one aligned 32-bit word, two mask words each.
+  // With SIGNS_LDS the 8 MT words of a lane live in LDS as [w / 4][lane][4]
+  // (16-byte reads of consecutive lanes: no bank conflicts), written once
+  // by wave 0 before any wave may leave.
+  constexpr int NMASK = SIGNS_LDS ? 1 : MT;
+  unsigned smask[NMASK][2][2][2];
+  const bool have_signs = signs != nullptr;
+  if constexpr (SIGNS_LDS) {
+    if (have_signs && wave == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            unsigned m0, m1;
+            sign_masks4(*(const unsigned *)(signs + 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m), m0, m1);
+            const int w = ((m * 2 + s) * 2 + h) * 2;   // words w, w + 1
+            sign_lds[((w >> 2) * 64 + lane) * 4 + (w & 3)] = m0;
+            sign_lds[(((w + 1) >> 2) * 64 + lane) * 4 + ((w + 1) & 3)] = m1;
+          }
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          smask[m][s][h][0] = smask[m][s][h][1] = 0u;
+          if (have_signs)
+            sign_masks4(*(const unsigned *)(signs + 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m),
+                        smask[m][s][h][0], smask[m][s][h][1]);
+        }
+  }
   if (wave_id >= rows) return;
 
   // DMA of row r into buffer b.  Rows past the end are clamped to the last
@@ -153,35 +214,24 @@ __global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
   };
 
   issue_row(wave_id, 0);
-  issue_row(wave_id + wave_stride, 1);
+  if constexpr (kBufs == 2) issue_row(wave_id + wave_stride, 1);
 
-  // Sign masks for the pieces this lane reads: piece (m, s, h) covers
-  // elements base + 0..3 with base = 4 c16 + 64 g + 256 h + 512 s + 1024 m;
-  // their four int8 signs are one aligned 32-bit word.
-  unsigned smask[MT][2][2][2];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        smask[m][s][h][0] = smask[m][s][h][1] = 0u;
-        if (signs != nullptr)
-          sign_masks4(*(const unsigned *)(signs + 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m),
-                      smask[m][s][h][0], smask[m][s][h][1]);
-      }
-
-  wait_vm<0>();   // the sign words (and the first two rows) are in: no wait on them inside the loop
+  wait_vm<0>();   // the sign words (and the first rows) are in: no wait on them inside the loop
 
   int it = 0;
   for (int64_t row = wave_id; row < rows; row += wave_stride, ++it) {
-    const uint8_t *buf = bufs + (it & 1) * ROWB;
-    // Wait for this row's DMA.  Issued after it: the DMA of the following
-    // row (always), the stores of the previous row (it >= 1) and of the one
-    // before, with the DMA of this row's follower in between (it >= 2).
-    if (it == 0) wait_vm<DMA>();
-    else if (it == 1) wait_vm<DMA + STORES>();
-    else wait_vm<DMA + 2 * STORES>();
+    const uint8_t *buf = bufs + (kBufs == 2 ? (it & 1) * ROWB : 0);
+    // Wait for this row's DMA.  Two buffers: issued after it are the DMA of
+    // the following row (always), the stores of the previous row (it >= 1)
+    // and of the one before, with the DMA of this row's follower in between
+    // (it >= 2).  One buffer: only the previous row's stores (it >= 1).
+    if constexpr (kBufs == 2) {
+      if (it == 0) wait_vm<DMA>();
+      else if (it == 1) wait_vm<DMA + STORES>();
+      else wait_vm<DMA + 2 * STORES>();
+    } else {
+      if (it > 0) wait_vm<STORES>();
+    }
 
     // ---- pass 1: 64-point factor on MFMA, A read from the LDS row buffer
     v2u pc[MT][2][2];
@@ -192,9 +242,23 @@ __global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           pc[m][s][h] = *(const v2u *)(buf + 2 * (4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m));
-    // every read has returned: the buffer takes the row after next
+    if constexpr (SIGNS_LDS) {
+      if (have_signs) {
+#pragma unroll
+        for (int q = 0; q < 2 * MT; ++q) {   // 4 words per read: pieces (m, s) = q, h = 0, 1
+          const v4u mw = *(const v4u *)(sign_lds + (q * 64 + lane) * 4);
+          const int m = q >> 1, s = q & 1;
+          pc[m][s][0][0] ^= mw[0];
+          pc[m][s][0][1] ^= mw[1];
+          pc[m][s][1][0] ^= mw[2];
+          pc[m][s][1][1] ^= mw[3];
+        }
+      }
+    }
+    // every read has returned: the buffer takes its next row
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    issue_row(row + 2 * wave_stride, it & 1);
+    if constexpr (kBufs == 2) issue_row(row + 2 * wave_stride, it & 1);
+    else issue_row(row + wave_stride, 0);
 
     float v[NV];
 #pragma unroll
@@ -203,10 +267,17 @@ __global__ __launch_bounds__(64 * kWaves) void rq_pow2_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         v4u w;
-        w[0] = pc[m][s][0][0] ^ smask[m][s][0][0];
-        w[1] = pc[m][s][0][1] ^ smask[m][s][0][1];
-        w[2] = pc[m][s][1][0] ^ smask[m][s][1][0];
-        w[3] = pc[m][s][1][1] ^ smask[m][s][1][1];
+        if constexpr (SIGNS_LDS) {
+          w[0] = pc[m][s][0][0];
+          w[1] = pc[m][s][0][1];
+          w[2] = pc[m][s][1][0];
+          w[3] = pc[m][s][1][1];
+        } else {
+          w[0] = pc[m][s][0][0] ^ smask[m][s][0][0];
+          w[1] = pc[m][s][0][1] ^ smask[m][s][0][1];
+          w[2] = pc[m][s][1][0] ^ smask[m][s][1][0];
+          w[3] = pc[m][s][1][1] ^ smask[m][s][1][1];
+        }
         a[s] = __builtin_bit_cast(v8h, w);
       }
 #pragma unroll
@@ -335,11 +406,13 @@ hipError_t launch_one(const void *x, int64_t rows, int64_t ld_x, const int8_t *s
   static int per_cu = 0;
   if (per_cu == 0) {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rq_pow2_kernel<L, GROUP, BITS>, 64 * kWaves, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rq_pow2_kernel<L, GROUP, BITS>, 64 * waves_of<L>(), 0) !=
+            hipSuccess ||
         b < 1)
       b = 1;
     per_cu = b;
   }
+  constexpr int kWaves = waves_of<L>();
   const int64_t blocks_needed = (rows + kWaves - 1) / kWaves;
   const int64_t cap = (int64_t)cus * per_cu;
   const int64_t grid = blocks_needed < cap ? blocks_needed : cap;
