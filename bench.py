@@ -1,10 +1,15 @@
 #!/usr/bin/env python3
 """Throughput of QuaRot's 4-bit linear-layer hot path on one MI355X.
 
-One step = one pass of the whole path over one batch, all on one HIP stream:
+One step = one pass of the whole path over one batch, in order on one HIP
+stream:
   qr_rotate_quant  x [M, K] fp16 -> int4 codes + per-token scales
   qr_int4_gemm     codes x pre-rotated int4 weights -> y [M, N] fp16
   qr_kv_quant      the K and V slices of y (fused QKV output), 32 heads x 128
+Consecutive steps (independent batches) alternate over --streams HIP streams
+of default priority, so that one batch's small, latency-bound kernels run
+beside another batch's GEMM; a buffer set is reused only after the step that
+last used it has finished (an event dependency).
 Default workload: LLaMA-2-7B fused QKV prefill, x 2048 x 4096 -> 12288 (the
 layer the QuaRot summary's prefill figures are about: batch 64 x 2048 tokens
 in one block).  Inputs are synthetic and seeded (package ``workloads``);
@@ -19,7 +24,7 @@ average launch time from HIP events recorded around each launch on the
 launch stream.  `cpu_baseline` is the CPU oracle timed on a bounded row
 sample of the same workload.
 
-  python bench.py [--steps 20] [--warmup 5] [--config c2] [--no-cpu]
+  python bench.py [--steps 20] [--warmup 5] [--config c2] [--streams 2] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -50,6 +55,8 @@ def parse():
     ap.add_argument("--config", default="c2", choices=["c2"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows in the CPU oracle sample (0 = all)")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="HIP streams the steps alternate over (1: strictly one step after another)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to cycle (0 = enough for 1 GiB)")
@@ -400,22 +407,44 @@ def main():
         sets.append(s)
     del x0, wc0, ws0
     stream = torch.cuda.current_stream()
+    # default-priority streams only
+    streams = [stream] + [torch.cuda.Stream(device=dev) for _ in range(max(1, args.streams) - 1)]
 
-    def rq(s):
-        qr.rotate_quant(s["x"], rot, cfg.group, codes=s["xc"], scales=s["xs"], stream=stream)
+    def rq(s, st=stream):
+        qr.rotate_quant(s["x"], rot, cfg.group, codes=s["xc"], scales=s["xs"], stream=st)
 
-    def gemm(s):
-        qr.int4_gemm(s["xc"], s["xs"], s["wc"], s["ws"], cfg.group, y=s["y"], stream=stream)
+    def gemm(s, st=stream):
+        qr.int4_gemm(s["xc"], s["xs"], s["wc"], s["ws"], cfg.group, y=s["y"], stream=st)
 
-    def kv(s):
+    def kv(s, st=stream):
         # K and V are adjacent column ranges of the QKV output: one launch
         # quantizes the 2H head vectors of every token
-        qr.kv_quant(s["y"][:, K:3 * K], codes=s["kvc"], scales=s["kvs"], zeros=s["kvz"], stream=stream)
+        qr.kv_quant(s["y"][:, K:3 * K], codes=s["kvc"], scales=s["kvs"], zeros=s["kvz"], stream=st)
 
-    def step(s):
-        rq(s)
-        gemm(s)
-        kv(s)
+    def step(i):
+        s = sets[i % nsets]
+        st = streams[i % len(streams)]
+        if "done" in s and s["done_on"] is not st:
+            st.wait_event(s["done"])   # the set's previous step, on another stream, has finished
+        rq(s, st)
+        gemm(s, st)
+        kv(s, st)
+        if len(streams) > 1:
+            s["done"] = torch.cuda.Event()
+            s["done"].record(st)
+            s["done_on"] = st
+
+    def fork():
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        for st in streams[1:]:
+            st.wait_event(ev)
+
+    def join():
+        for st in streams[1:]:
+            ev = torch.cuda.Event()
+            ev.record(st)
+            stream.wait_event(ev)
 
     if args.copy_calib:
         nb = args.copy_calib << 20
@@ -425,8 +454,10 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    fork()
     for i in range(args.warmup):
-        step(sets[i % nsets])
+        step(i)
+    join()
     torch.cuda.synchronize()
 
     # the timed region: exactly `steps` steps, nothing else on the stream
@@ -435,8 +466,10 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
+    fork()
     for i in range(args.steps):
-        step(sets[i % nsets])
+        step(i)
+    join()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -475,7 +508,7 @@ def main():
             "workload": f"{cfg.name}: {cfg.desc}; rotate D.H_{K} + per-token int4 RTN, int4 GEMM (int8 MFMA, "
                         f"per-channel int4 weights, fp16 out), 4-bit KV quant of the K and V heads (one launch, {M}x{2 * H}x128)",
             "M": M, "N": N, "K": K, "group": cfg.group, "codes": "int4", "mfma": "int8 -> int32",
-            "rotation": "fp32 (fp16-MFMA first factor)", "buffer_sets": nsets,
+            "rotation": "fp32 (fp16-MFMA first factor)", "buffer_sets": nsets, "streams": len(streams),
         },
         "kernels": {
             "rotate_quant": {"us": round(rq_ms * 1e3, 3), "GB/s": round(rq_bytes / (rq_ms * 1e-3) / 1e9, 1),
