@@ -53,6 +53,10 @@ Readings where the pages are silent (each repeated where it is used):
   R20 6- and 8-bit variants: the same symmetric RTN with qmax = 2^(b-1) - 1
      (31, 127) in place of 7; codes stored one per byte (int8) and multiplied
      as int8, no packing.
+  R21 The activation feeding down_proj, fused before the rotation: LLaMA-2's
+     gated FFN activation x = silu(gate) * up, silu(g) = g / (1 + e^-g),
+     rounded to fp16 (the value an unfused pipeline would hand on), then
+     rotated and quantized as any activation row.
 """
 from __future__ import annotations
 
@@ -63,7 +67,7 @@ __all__ = [
     "quantize_symmetric", "pack_int4", "unpack_int4", "unpack_uint4",
     "rotate_weights", "quantize_weights", "int_gemm", "dequantize_output",
     "dequantize_symmetric", "linear_w4a4", "kv_quantize", "kv_dequantize",
-    "kv_attention_decode",
+    "kv_attention_decode", "silu", "swiglu_fp16",
 ]
 
 
@@ -239,6 +243,21 @@ def unpack_uint4(b: np.ndarray) -> np.ndarray:
     """Inverse of pack_int4 for unsigned codes: uint8 in [0, 15]."""
     b = np.asarray(b, dtype=np.int64)
     return np.stack([b & 0xF, b >> 4], axis=-1).reshape(*b.shape[:-1], b.shape[-1] * 2).astype(np.uint8)
+
+
+def silu(g) -> np.ndarray:
+    """silu(g) = g / (1 + exp(-g)) in fp64 (the gate nonlinearity of LLaMA-2's
+    feed-forward block; R21)."""
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu_fp16(gate, up) -> np.ndarray:
+    """x = fp16(silu(gate) * up): the feed-forward activation whose rotation
+    and quantization the fused call performs (R21; [QuaRot-abs]: the
+    activations of the feed-forward components are rotated as well).  fp16
+    round to nearest even of the fp64 product."""
+    return (silu(gate) * np.asarray(up, dtype=np.float64)).astype(np.float16)
 
 
 # --------------------------------------------------------------------------

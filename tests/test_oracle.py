@@ -603,3 +603,29 @@ def test_rtn_6_8_bits_near_lossless():
     assert err[8] < 0.015 and err[6] < 0.05 and err[4] > 0.1
     assert 2.5 < err[4] / err[6] < 6 and 2.5 < err[6] / err[8] < 6
     assert all(err[b] < plain[b] for b in (4, 6, 8))
+
+
+# ------------------------------------------------- fused feed-forward activation
+
+def test_silu_closed_forms():
+    """silu(0) = 0; silu(g) - silu(-g) = g (since sigma(g) + sigma(-g) = 1);
+    silu(ln 3) = (3/4) ln 3; silu -> g for large g, -> 0 for very negative g."""
+    g = np.linspace(-9, 9, 37)
+    assert O.silu(0.0) == 0.0
+    assert np.allclose(O.silu(g) - O.silu(-g), g, rtol=0, atol=1e-14)
+    assert O.silu(np.log(3)) == pytest.approx(0.75 * np.log(3), rel=1e-15)
+    assert O.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert abs(O.silu(-40.0)) < 1e-15
+
+
+def test_swiglu_fp16_rounding():
+    """The product is rounded once, to the nearest fp16: exact cases stay
+    exact (silu(ln 3) * 4 / ln 3 = 3, silu(0) * 7 = 0); 30 (1 + 2^-11) =
+    30.0146... lies 0.00098 below the fp16 neighbour 30.015625 (fp16 spacing
+    at 30 is 2^-6) and 0.0146 above 30, so it rounds up."""
+    g = np.array([np.log(3), 0.0, 40.0])
+    u = np.array([4 / np.log(3), 7.0, 0.75 * (1.0 + 2 ** -11)])   # silu(40) = 40 in fp64
+    x = O.swiglu_fp16(g, u)
+    assert x.dtype == np.float16
+    assert x[0] == np.float16(3.0) and x[1] == 0
+    assert float(x[2]) == 30.015625
