@@ -295,6 +295,19 @@ def suite(args):
              GBs=round(nbytes / ms / 1e6, 1), frac_hbm=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
              bytes=nbytes, buffers=len(xs))
 
+    def swiglu_case(name, cfg, rows, reps=3):
+        if only and name not in only:
+            return
+        c = W.CONFIGS[cfg]
+        gu = torch.randn((rows, 2 * c.K), device=dev, generator=g).half()   # fused gate/up output [rows, 2n]
+        rot = qr.Rotation.kronecker(c.had_n, W.make_dense(c), W.make_signs(c))
+        out = qr.swiglu_rotate_quant(gu[:, :c.K], gu[:, c.K:], rot)
+        ms = time_each(lambda i: qr.swiglu_rotate_quant(gu[:, :c.K], gu[:, c.K:], rot, 0, *out), reps,
+                       torch.cuda.current_stream())
+        nbytes = rows * c.K * 4 + rows * c.K // 2 + rows * 4
+        emit(name, kernel="qr_swiglu_rotate_quant", shape=[rows, c.K], us=round(ms * 1e3, 3),
+             GBs=round(nbytes / ms / 1e6, 1), frac_hbm=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), bytes=nbytes)
+
     def kv_case(name, T, reps=20, cycle=True):
         if only and name not in only:
             return
@@ -344,6 +357,7 @@ def suite(args):
     gemm_case("gemm_c5_decode_streamed", 64, 4096, 4096, 0, reps=128, stream_w=64)
     kv_case("kv_c5_decode", 64, reps=50, cycle=False)
     kv_case("kv_prefill_131072", 131072, reps=5)
+    swiglu_case("swiglu_rq_d70", "d70", 16384)
     gemm8_case("gemm8_c2", 2048, 12288, 4096, 0)
     gemm8_case("gemm8_c4_g128", 16384, 28672, 8192, 128, reps=3)
     gemm8_case("gemm8_c5_decode", 64, 4096, 4096, 0, reps=50)

@@ -132,6 +132,24 @@ qr_status qr_int4_gemm(const uint8_t *a_codes, const float *a_scales,
                        void *y_f16, int64_t ld_y, void *stream);
 
 /*
+ * qr_rotate_quant of the feed-forward activation that feeds down_proj,
+ * formed on the fly (QuaRot abstract: the activations of the feed-forward
+ * components are rotated too): row r is
+ *   x = fp16(silu(gate[r, :]) * up[r, :]),   silu(g) = g / (1 + e^-g)
+ * in fp32 with one fp16 rounding, then rotated, quantized and packed as by
+ * qr_rotate_quant.  x itself is never written.
+ * gate_f16, up_f16  device fp16, row r at ptr + r * ld (elements), 16-byte
+ *                   aligned; ld >= n, a multiple of 8 (e.g. the two halves of
+ *                   a fused gate/up projection output [rows][2n], ld = 2n).
+ * All other arguments as for qr_rotate_quant.  n = 4096 * m (2 <= m <= 8, no
+ * signs, per row; 28672 for LLaMA-2-70B) runs the MFMA kernel; other
+ * rotations run the reference-shape kernel.
+ */
+qr_status qr_swiglu_rotate_quant(const void *gate_f16, const void *up_f16, int64_t rows, int64_t ld,
+                                 const qr_rotation *rot, int64_t group, uint8_t *codes,
+                                 float *scales, void *stream);
+
+/*
  * 6- and 8-bit variants (QuaRot abstract: plain round-to-nearest gives
  * lossless 6- and 8-bit models).  The same rotation and symmetric RTN with
  * qmax = 2^(bits-1) - 1 (31 or 127) in place of 7:

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "QRError", "LibraryNotBuilt", "Rotation", "library", "library_path", "rotate_quant", "int4_gemm",
     "int4_gemm_i32", "kv_quant", "kv_attn_decode", "kv_attn_decode_workspace", "rotate_quant_i8",
-    "int8_gemm", "int8_gemm_i32", "status_str", "version", "EXPORTS",
+    "int8_gemm", "int8_gemm_i32", "swiglu_rotate_quant", "status_str", "version", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +32,7 @@ _lib = None
 QR_OK, QR_EINVAL, QR_ESHAPE, QR_EALIGN, QR_EDEVICE = 0, 1, 2, 3, 4
 EXPORTS = ("qr_rotate_quant", "qr_int4_gemm", "qr_kv_quant", "qr_int4_gemm_i32", "qr_kv_attn_decode",
            "qr_kv_attn_decode_workspace", "qr_rotate_quant_i8", "qr_int8_gemm", "qr_int8_gemm_i32",
-           "qr_status_str", "qr_version")
+           "qr_swiglu_rotate_quant", "qr_status_str", "qr_version")
 
 
 class QRError(RuntimeError):
@@ -82,6 +82,8 @@ def library():
     lib.qr_int8_gemm.restype = st
     lib.qr_int8_gemm_i32.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp]
     lib.qr_int8_gemm_i32.restype = st
+    lib.qr_swiglu_rotate_quant.argtypes = [vp, vp, i64, i64, ctypes.POINTER(_Rot), i64, vp, vp, vp]
+    lib.qr_swiglu_rotate_quant.restype = st
     lib.qr_status_str.argtypes = [st]
     lib.qr_status_str.restype = ctypes.c_char_p
     lib.qr_version.argtypes = []
@@ -349,3 +351,30 @@ def int8_gemm_i32(a_codes, w_codes, group: int = 0, acc=None, stream=None):
                                     _stream(stream))
     _check("qr_int8_gemm_i32", st)
     return acc
+
+
+def swiglu_rotate_quant(gate: torch.Tensor, up: torch.Tensor, rot: Rotation, group: int = 0, codes=None,
+                        scales=None, stream=None):
+    """qr_swiglu_rotate_quant: rotate and quantize x = fp16(silu(gate) * up)
+    without forming x.  gate and up fp16 [rows, >= n] with unit column stride
+    and the same row stride (e.g. two column halves of one [rows, 2n] tensor).
+    Returns (codes uint8 [rows, n/2], scales fp32 [rows] or [rows, n/group])."""
+    _need(gate, torch.float16, "gate")
+    _need(up, torch.float16, "up")
+    if gate.dim() != 2 or up.dim() != 2 or gate.stride(1) != 1 or up.stride(1) != 1 or gate.shape != up.shape:
+        raise ValueError("gate and up must be 2-D, equal in shape, with unit column stride")
+    rows = gate.shape[0]
+    ld = gate.stride(0) if rows > 1 else max(gate.stride(0), rot.n + (-rot.n) % 8)
+    if rows > 1 and up.stride(0) != ld:
+        raise ValueError("gate and up must share one row stride")
+    if codes is None:
+        codes = torch.empty((rows, rot.n // 2), dtype=torch.uint8, device=gate.device)
+    if scales is None:
+        scales = torch.empty((rows,) if group == 0 else (rows, rot.n // group), dtype=torch.float32,
+                             device=gate.device)
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.float32, "scales")
+    st = library().qr_swiglu_rotate_quant(_ptr(gate), _ptr(up), rows, ld, ctypes.byref(rot._c), int(group),
+                                          _ptr(codes), _ptr(scales), _stream(stream))
+    _check("qr_swiglu_rotate_quant", st)
+    return codes, scales

@@ -101,6 +101,28 @@ qr_status qr_rotate_quant_i8(const void *x_f16, int64_t rows, int64_t ld_x, cons
       qr::launch_rq_generic_bits(x_f16, rows, ld_x, r, (int)group, (int)bits, (uint8_t *)codes, scales, s));
 }
 
+qr_status qr_swiglu_rotate_quant(const void *gate_f16, const void *up_f16, int64_t rows, int64_t ld,
+                                 const qr_rotation *rot, int64_t group, uint8_t *codes, float *scales,
+                                 void *stream) {
+  qr_status st = check_rotation(rot);
+  if (st != QR_OK) return st;
+  if (rows < 0) return QR_EINVAL;
+  if (group != 0 && (group < 32 || !pow2(group) || rot->n % group != 0)) return QR_ESHAPE;
+  if (ld < rot->n) return QR_ESHAPE;
+  if (ld % 8 != 0) return QR_EALIGN;
+  if (rows == 0) return QR_OK;
+  if (gate_f16 == nullptr || up_f16 == nullptr || codes == nullptr || scales == nullptr) return QR_EINVAL;
+  if (!aligned(gate_f16, 16) || !aligned(up_f16, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return QR_EALIGN;
+  if (rot->signs != nullptr && !aligned(rot->signs, 4)) return QR_EALIGN;
+
+  qr::RotArgs r{(int)rot->n, (int)rot->had_n, (int)rot->dense_m, rot->dense, rot->signs};
+  hipStream_t s = (hipStream_t)stream;
+  if (qr::rq_kron4096_supported(r, (int)group))
+    return from_hip(qr::launch_swiglu_rq_kron4096(gate_f16, up_f16, rows, ld, r, codes, scales, s));
+  return from_hip(qr::launch_rq_generic_full(gate_f16, up_f16, rows, ld, r, (int)group, 4, codes, scales, s));
+}
+
 qr_status qr_int8_gemm(const int8_t *a_codes, const float *a_scales, const int8_t *w_codes,
                        const float *w_scales, int64_t M, int64_t N, int64_t K, int64_t group, void *y_f16,
                        int64_t ld_y, void *stream) {

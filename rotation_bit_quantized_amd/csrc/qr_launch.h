@@ -22,6 +22,9 @@ hipError_t launch_rq_generic(const void *x, int64_t rows, int64_t ld_x, const Ro
 // bits 4 (packed) or 6, 8 (int8 codes, one per byte)
 hipError_t launch_rq_generic_bits(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group, int bits,
                                   uint8_t *codes, float *scales, hipStream_t stream);
+// ... with x = fp16(silu(x) * up) formed on the fly when up != nullptr
+hipError_t launch_rq_generic_full(const void *x, const void *up, int64_t rows, int64_t ld_x, const RotArgs &r,
+                                  int group, int bits, uint8_t *codes, float *scales, hipStream_t stream);
 
 // Rotate + quantize for n in {4096, 8192}, no dense factor, group 0 or 128
 // (first Hadamard factor on fp16 MFMA, the rest in registers, one wave per row).
@@ -42,6 +45,9 @@ hipError_t launch_rq_kron(const void *x, int64_t rows, int64_t ld_x, const RotAr
 bool rq_kron4096_supported(const RotArgs &r, int group);
 hipError_t launch_rq_kron4096(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, uint8_t *codes,
                               float *scales, hipStream_t stream);
+// the same with the row formed as fp16(silu(gate) * up)
+hipError_t launch_swiglu_rq_kron4096(const void *gate, const void *up, int64_t rows, int64_t ld, const RotArgs &r,
+                                     uint8_t *codes, float *scales, hipStream_t stream);
 
 // Integer GEMM.  out_i32 == false: fp16 output with ld_y; true: int32 sums.
 hipError_t launch_gemm_prefill(const uint8_t *a, const float *sa, const uint8_t *w, const float *sw,

@@ -2,6 +2,8 @@
 //
 // One workgroup owns one token row at a time (grid-stride over rows).  The
 // row is staged in LDS as fp32:
+//   0. (fused call) x = fp16(silu(gate) * up): the feed-forward activation
+//      before down_proj, formed here instead of being read
 //   1. x * signs                       (the random diagonal D, input side)
 //   2. dense factor: t[i*m + b] = sum_a x[i*m + a] O[a][b]   (if m > 1)
 //   3. Walsh-Hadamard butterflies over the Hadamard index i, in place
@@ -28,7 +30,8 @@ constexpr int kBlock = 256;
 constexpr int kInPlaceM = 16;   // dense factors up to this size are applied in place
 
 __global__ __launch_bounds__(kBlock) void rq_generic_kernel(
-    const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, int n, int had_n, int dense_m,
+    const unsigned short *__restrict__ x, const unsigned short *__restrict__ up, int64_t rows, int64_t ld_x, int n,
+    int had_n, int dense_m,
     const float *__restrict__ dense, const int8_t *__restrict__ signs, int group, int qmax,
     uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
   extern __shared__ float smem[];
@@ -45,8 +48,13 @@ __global__ __launch_bounds__(kBlock) void rq_generic_kernel(
 
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const unsigned short *xr = x + row * ld_x;
+    const unsigned short *ur = up != nullptr ? up + row * ld_x : nullptr;
     for (int k = tid; k < n; k += kBlock) {
       float v = half_bits_to_float(xr[k]);
+      if (ur != nullptr) {   // x = fp16(silu(gate) * up)
+        const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * v);
+        v = (float)(_Float16)(v * __builtin_amdgcn_rcpf(1.0f + e) * half_bits_to_float(ur[k]));
+      }
       if (signs != nullptr && signs[k] < 0) v = -v;
       buf[k] = v;
     }
@@ -145,6 +153,11 @@ hipError_t launch_rq_generic(const void *x, int64_t rows, int64_t ld_x, const Ro
 
 hipError_t launch_rq_generic_bits(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group, int bits,
                                   uint8_t *codes, float *scales, hipStream_t stream) {
+  return launch_rq_generic_full(x, nullptr, rows, ld_x, r, group, bits, codes, scales, stream);
+}
+
+hipError_t launch_rq_generic_full(const void *x, const void *up, int64_t rows, int64_t ld_x, const RotArgs &r,
+                                  int group, int bits, uint8_t *codes, float *scales, hipStream_t stream) {
   const int qmax = (1 << (bits - 1)) - 1;
   const int g = group ? group : r.n;
   const bool two_copies = r.dense_m > kInPlaceM;
@@ -157,7 +170,8 @@ hipError_t launch_rq_generic_bits(const void *x, int64_t rows, int64_t ld_x, con
   const int64_t grid = rows < 4096 ? rows : 4096;
   const float scale_mul = (float)(1.0 / ((double)qmax * __builtin_sqrt((double)r.had_n)));
   rq_generic_kernel<<<dim3((unsigned)grid), dim3(kBlock), lds, stream>>>(
-      (const unsigned short *)x, rows, ld_x, r.n, r.had_n, r.dense_m, r.dense, r.signs, group, qmax, codes,
+      (const unsigned short *)x, (const unsigned short *)up, rows, ld_x, r.n, r.had_n, r.dense_m, r.dense, r.signs,
+      group, qmax, codes,
       scales, scale_mul);
   return hipGetLastError();
 }

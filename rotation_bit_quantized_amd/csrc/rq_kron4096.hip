@@ -33,6 +33,14 @@
 //    packed eight to a word; a 4 x 4 nibble transpose within lane quads
 //    turns each 16-bit half into four consecutive codes of one output block,
 //    staged in LDS in the output layout and stored as 16-byte chunks.
+//
+// FUSED: the row is the feed-forward activation x = fp16(silu(gate) * up)
+// of the block before down_proj (QuaRot abstract: the feed-forward
+// activations are rotated too).  The gate row arrives by DMA as x would;
+// right after it lands, every thread loads its pieces of the up row from
+// global memory (coalesced, 16 bytes each) and rewrites the row in LDS as
+// x (fp32 arithmetic, one fp16 rounding), so the fused call reads gate and
+// up once and never writes x.
 #include "qr_common.h"
 #include "qr_launch.h"
 
@@ -44,10 +52,24 @@ constexpr int kMT = 32;       // M-tiles of 16 blocks: t < 512
 constexpr int kKS = 2;        // k-steps of 32: block width 8 M <= 64
 constexpr int kGrp = 4;       // M-tiles per A-read group
 
-template <int M>
+// silu(g) u in fp32 for the two fp16 halves of a word, rounded to fp16.
+__device__ __forceinline__ unsigned swiglu2(unsigned gw, unsigned uw) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 g = __builtin_bit_cast(h2, gw), u = __builtin_bit_cast(h2, uw);
+  h2 r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float gf = (float)g[k];
+    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * gf);   // e^-g
+    r[k] = (_Float16)(gf * __builtin_amdgcn_rcpf(1.0f + e) * (float)u[k]);
+  }
+  return __builtin_bit_cast(unsigned, r);
+}
+
+template <int M, bool FUSED>
 __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron4096_kernel(
-    const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, const float *__restrict__ dense,
-    uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
+    const unsigned short *__restrict__ x, const unsigned short *__restrict__ up, int64_t rows, int64_t ld_x,
+    const float *__restrict__ dense, uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
   static_assert(M >= 2 && M <= 8, "dense factor size");
   constexpr int kRowBytes = 8192 * M;        // 4096 M fp16
   constexpr int kBlkBytes = 16 * M;          // one block t: 8 M fp16
@@ -123,14 +145,36 @@ __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron4096_kernel(
   int64_t row = blockIdx.x;   // the grid is no larger than rows
   issue_row(row);
   bool first = true;
+  constexpr int kPieces = FUSED ? kRowBytes / 16 / (64 * kWaves) : 1;   // 16-byte pieces of up per thread
   for (; row < rows; row += stride) {
+    // FUSED: this row's up pieces, loaded while the gate row's DMA finishes
+    v4u uv[kPieces];
+    if constexpr (FUSED) {
+      const uint8_t *ur = (const uint8_t *)(up + row * ld_x);
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p) uv[p] = *(const v4u *)(ur + 16 * (tid + 64 * kWaves * p));
+    }
     // this row's DMA; issued after it (except for the first row): the
-    // previous row's kPerThread chunk stores (and one scale store)
+    // previous row's kPerThread chunk stores (and one scale store), then
+    // the up pieces
     if (first) wait_vm<0>();
-    else wait_vm<kPerThread>();
+    else wait_vm<kPerThread + (FUSED ? kPieces : 0)>();
     first = false;
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
+
+    if constexpr (FUSED) {
+      // the gate row is in xrow: rewrite it as x = silu(gate) up
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p) {
+        v4u *px = (v4u *)(xrow + 16 * (tid + 64 * kWaves * p));
+        const v4u gv = *px;
+        *px = v4u{swiglu2(gv[0], uv[p][0]), swiglu2(gv[1], uv[p][1]), swiglu2(gv[2], uv[p][2]),
+                  swiglu2(gv[3], uv[p][3])};
+      }
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+    }
 
     // ---- Z = X B for this wave's 16 columns, all 512 blocks
     v4f c[kMT];
@@ -254,16 +298,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron4096_kernel(
   wait_vm<0>();   // no DMA may still be writing this block's LDS when it exits
 }
 
-template <int M>
-hipError_t launch_m(const void *x, int64_t rows, int64_t ld_x, const float *dense, uint8_t *codes, float *scales,
-                    hipStream_t stream) {
+template <int M, bool FUSED>
+hipError_t launch_m(const void *x, const void *up, int64_t rows, int64_t ld_x, const float *dense, uint8_t *codes,
+                    float *scales, hipStream_t stream) {
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   static int per_cu = 0;
   if (per_cu == 0) {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rq_kron4096_kernel<M>, 64 * kWaves, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rq_kron4096_kernel<M, FUSED>, 64 * kWaves, 0) != hipSuccess ||
         b < 1)
       b = 1;
     per_cu = b;
@@ -271,8 +315,8 @@ hipError_t launch_m(const void *x, int64_t rows, int64_t ld_x, const float *dens
   const int64_t cap = (int64_t)cus * per_cu;
   const int64_t grid = rows < cap ? rows : cap;
   const float scale_mul = (float)(1.0 / (7.0 * 64.0));   // 1/(7 sqrt(4096))
-  rq_kron4096_kernel<M><<<dim3((unsigned)grid), dim3(64 * kWaves), 0, stream>>>(
-      (const unsigned short *)x, rows, ld_x, dense, codes, scales, scale_mul);
+  rq_kron4096_kernel<M, FUSED><<<dim3((unsigned)grid), dim3(64 * kWaves), 0, stream>>>(
+      (const unsigned short *)x, (const unsigned short *)up, rows, ld_x, dense, codes, scales, scale_mul);
   return hipGetLastError();
 }
 
@@ -282,17 +326,28 @@ bool rq_kron4096_supported(const RotArgs &r, int group) {
   return r.had_n == 4096 && r.dense_m >= 2 && r.dense_m <= 8 && r.signs == nullptr && group == 0;
 }
 
+template <bool FUSED>
+hipError_t launch_fused_or_not(const void *x, const void *up, int64_t rows, int64_t ld_x, const RotArgs &r,
+                               uint8_t *codes, float *scales, hipStream_t stream) {
+  switch (r.dense_m) {
+    case 2: return launch_m<2, FUSED>(x, up, rows, ld_x, r.dense, codes, scales, stream);
+    case 3: return launch_m<3, FUSED>(x, up, rows, ld_x, r.dense, codes, scales, stream);
+    case 4: return launch_m<4, FUSED>(x, up, rows, ld_x, r.dense, codes, scales, stream);
+    case 5: return launch_m<5, FUSED>(x, up, rows, ld_x, r.dense, codes, scales, stream);
+    case 6: return launch_m<6, FUSED>(x, up, rows, ld_x, r.dense, codes, scales, stream);
+    case 7: return launch_m<7, FUSED>(x, up, rows, ld_x, r.dense, codes, scales, stream);
+    default: return launch_m<8, FUSED>(x, up, rows, ld_x, r.dense, codes, scales, stream);
+  }
+}
+
 hipError_t launch_rq_kron4096(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, uint8_t *codes,
                               float *scales, hipStream_t stream) {
-  switch (r.dense_m) {
-    case 2: return launch_m<2>(x, rows, ld_x, r.dense, codes, scales, stream);
-    case 3: return launch_m<3>(x, rows, ld_x, r.dense, codes, scales, stream);
-    case 4: return launch_m<4>(x, rows, ld_x, r.dense, codes, scales, stream);
-    case 5: return launch_m<5>(x, rows, ld_x, r.dense, codes, scales, stream);
-    case 6: return launch_m<6>(x, rows, ld_x, r.dense, codes, scales, stream);
-    case 7: return launch_m<7>(x, rows, ld_x, r.dense, codes, scales, stream);
-    default: return launch_m<8>(x, rows, ld_x, r.dense, codes, scales, stream);
-  }
+  return launch_fused_or_not<false>(x, nullptr, rows, ld_x, r, codes, scales, stream);
+}
+
+hipError_t launch_swiglu_rq_kron4096(const void *gate, const void *up, int64_t rows, int64_t ld, const RotArgs &r,
+                                     uint8_t *codes, float *scales, hipStream_t stream) {
+  return launch_fused_or_not<true>(gate, up, rows, ld, r, codes, scales, stream);
 }
 
 }  // namespace qr

@@ -218,3 +218,17 @@ def test_i8_rejects():
     assert gemm(M=0) == qr.QR_OK
     assert lib.qr_int8_gemm_i32(A16, A16, 128, 128, 512, 0, None, None) == qr.QR_EINVAL
     assert lib.qr_int8_gemm_i32(A16, A16, 128, 128, 512, 0, MIS, None) == qr.QR_EALIGN
+
+
+def test_swiglu_rejects():
+    lib = qr.library()
+    rot = qr._Rot(28672, 4096, 7, A16, None)
+    call = lambda g=A16, u=A16, ld=57344, rows=4: lib.qr_swiglu_rotate_quant(g, u, rows, ld, ctypes.byref(rot), 0,
+                                                                            A16, A16, None)
+    assert call(u=None) == qr.QR_EINVAL
+    assert call(g=None) == qr.QR_EINVAL
+    assert call(u=MIS) == qr.QR_EALIGN
+    assert call(ld=57340) == qr.QR_EALIGN
+    assert call(ld=28000) == qr.QR_ESHAPE
+    assert call(rows=-1) == qr.QR_EINVAL
+    assert call(rows=0, g=None, u=None) == qr.QR_OK
