@@ -202,11 +202,14 @@ __global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
   }
   if (wave_id >= rows) return;
 
-  // DMA of row r into buffer b.  Rows past the end are clamped to the last
-  // row (their buffers are never read), which keeps the number of vector
-  // memory instructions per row uniform and the vmcnt waits below exact.
+  // DMA of row r into buffer b.  Rows past the end re-read the wave's own
+  // first row (their buffers are never read), which keeps the number of
+  // vector memory instructions per row uniform and the vmcnt waits below
+  // exact; each wave re-reads a different row, so the redundant reads do not
+  // all converge on one address (with one row per wave, every wave's
+  // follower DMA used to hit the matrix's last row at once).
   auto issue_row = [&](int64_t r, int b) {
-    const uint8_t *src = (const uint8_t *)(x + (r < rows ? r : rows - 1) * ld_x);
+    const uint8_t *src = (const uint8_t *)(x + (r < rows ? r : wave_id) * ld_x);
 #pragma unroll
     for (int i = 0; i < DMA; ++i)
       __builtin_amdgcn_global_load_lds((const void *)(src + 1024 * i + 16 * lane),
