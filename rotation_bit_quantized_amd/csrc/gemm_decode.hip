@@ -8,12 +8,12 @@
 // memory; QuaRot press article: decoding is usually memory-bound).
 //
 // One workgroup (16 waves) owns 16 output channels and all M <= 64 tokens.
-// Wave w handles the K-units w, w + 16, ... (a unit is 64 codes per-channel,
-// or one 128-group); per unit it loads the 16 weight rows (8 bytes per lane)
-// and the 64 token rows (4 x 8 bytes per lane) straight into registers,
-// widens them to 16*q int8 (see gemm_prefill.hip) and issues
-// v_mfma_i32_16x16x64_i8 with A = weight rows, B = token rows, giving
-// C[channel][token].  The 16 per-wave partials are reduced through LDS in
+// Wave w handles the K-units w, w + 16, ... (a unit is one 64-byte piece of
+// each row per-channel, or one K-group); it loads up to four pieces at once
+// (16 weight rows and 64 token rows, 16 bytes per lane each) straight into
+// registers, so that one memory latency covers them, widens them to 16*q
+// int8 (see gemm_prefill.hip) and issues v_mfma_i32_16x16x64_i8 with
+// A = weight rows, B = token rows, giving C[channel][token].  The 16 per-wave partials are reduced through LDS in
 // int32 (per-channel, exact) or fp32 (group-wise, after scaling).
 //
 // 8-bit codes (CB = 8; the 6- and 8-bit RTN variants, QuaRot abstract): a
@@ -28,13 +28,18 @@ namespace {
 constexpr int kWaves = 16;
 constexpr int kNT = 16;  // output channels per workgroup
 
-__device__ __forceinline__ v4i widen8(v2u w) {
-  v4i op;
-  op[0] = (int)((w[0] << 4) & 0xF0F0F0F0u);
-  op[1] = (int)(w[0] & 0xF0F0F0F0u);
-  op[2] = (int)((w[1] << 4) & 0xF0F0F0F0u);
-  op[3] = (int)(w[1] & 0xF0F0F0F0u);
-  return op;
+// 32 packed codes (16 bytes) -> two MFMA operands of 16 int8 values 16 q
+// (the high-nibble form of the prefill kernel; the k order inside a dword
+// is permuted identically on both sides).
+__device__ __forceinline__ void widen16(const v4u &w, v4i &op0, v4i &op1) {
+  op0[0] = (int)((w[0] << 4) & 0xF0F0F0F0u);
+  op0[1] = (int)(w[0] & 0xF0F0F0F0u);
+  op0[2] = (int)((w[1] << 4) & 0xF0F0F0F0u);
+  op0[3] = (int)(w[1] & 0xF0F0F0F0u);
+  op1[0] = (int)((w[2] << 4) & 0xF0F0F0F0u);
+  op1[1] = (int)(w[2] & 0xF0F0F0F0u);
+  op1[2] = (int)((w[3] << 4) & 0xF0F0F0F0u);
+  op1[3] = (int)(w[3] & 0xF0F0F0F0u);
 }
 
 template <bool GROUPED, bool OUT_I32, int CB = 4>
@@ -51,14 +56,18 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
   static_assert(CB == 4 || CB == 8, "code width");
   constexpr int SHIFT = CB == 4 ? 8 : 0;           // widened 4-bit products carry 16 * 16
   constexpr float UNSCALE = CB == 4 ? 1.0f / 256.0f : 1.0f;
-  constexpr int STEP_BYTES = 64 * CB / 8;          // bytes of a 64-code step per row
+  // A piece is 64 bytes of a row: 128 4-bit or 64 8-bit codes, one 16-byte
+  // load per lane (lane >> 4 picks the quarter) and KS MFMA k-steps of 64.
+  constexpr int PIECE_CODES = 64 * 8 / CB;
+  constexpr int KS = CB == 4 ? 2 : 1;
+  constexpr int BATCH = GROUPED ? 2 : 4;            // pieces loaded together per wave (128 registers at most)
   const int64_t kbytes = (int64_t)K * CB / 8;
-  const int ksteps_per_unit = GROUPED ? group / 64 : 1;
-  const int units = K / 64 / ksteps_per_unit;
+  const int ppu = GROUPED ? group / PIECE_CODES : 1;   // pieces per unit (a unit: one K-group, or one piece)
+  const int units = K / PIECE_CODES / ppu;
   const int G = GROUPED ? K / group : 1;
 
   const int wrow = n0 + (lane & 15);                 // weight row (output channel) of this lane
-  const int kofs = (lane >> 4) * (STEP_BYTES / 4);   // byte offset of this lane's 16 codes in a 64-code step
+  const int kofs = (lane >> 4) * 16;                 // byte offset of this lane's quarter of a piece
   const bool wvalid = wrow < N;
   const uint8_t *wp = W + (int64_t)(wvalid ? wrow : 0) * kbytes + kofs;
   const uint8_t *ap[4];
@@ -72,54 +81,76 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
 
   v4i acc[4] = {v4i{}, v4i{}, v4i{}, v4i{}};
   v4f facc[4] = {v4f{}, v4f{}, v4f{}, v4f{}};
+  v4i uacc[4] = {v4i{}, v4i{}, v4i{}, v4i{}};
 
-  for (int u = wave; u < units; u += kWaves) {
-    v4i uacc[4] = {v4i{}, v4i{}, v4i{}, v4i{}};
-    for (int s = 0; s < ksteps_per_unit; ++s) {
-      const int64_t off = (int64_t)(u * ksteps_per_unit + s) * STEP_BYTES;
-      v4i wop, aop[4];
-      if constexpr (CB == 4) {
-        v2u wv = wvalid ? __builtin_nontemporal_load((const v2u *)(wp + off)) : v2u{0u, 0u};
-        wop = widen8(wv);
+  // This wave's pieces: units u = wave, wave + kWaves, ...; piece j of unit
+  // u is global piece u * ppu + j; flat index i = (unit ordinal) * ppu + j.
+  const int my_units = units > wave ? (units - wave + kWaves - 1) / kWaves : 0;
+  const int my_pieces = my_units * ppu;
+  for (int i0 = 0; i0 < my_pieces; i0 += BATCH) {
+    v4u wv[BATCH], av[BATCH][4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) aop[f] = widen8(avalid[f] ? *(const v2u *)(ap[f] + off) : v2u{0u, 0u});
-      } else {
-        wop = wvalid ? __builtin_nontemporal_load((const v4i *)(wp + off)) : v4i{};
+    for (int b = 0; b < BATCH; ++b) {   // all loads of the batch first: one memory latency
+      const int i = i0 + b;
+      const bool ok = i < my_pieces;
+      const int64_t off = ok ? ((int64_t)(wave + kWaves * (i / ppu)) * ppu + i % ppu) * 64 : 0;
+      wv[b] = ok && wvalid ? __builtin_nontemporal_load((const v4u *)(wp + off)) : v4u{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int f = 0; f < 4; ++f) aop[f] = avalid[f] ? *(const v4i *)(ap[f] + off) : v4i{};
-      }
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (GROUPED)
-          uacc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop[f], uacc[f], 0, 0, 0);
-        else
-          acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, aop[f], acc[f], 0, 0, 0);
-      }
+      for (int f = 0; f < 4; ++f) av[b][f] = ok && avalid[f] ? *(const v4u *)(ap[f] + off) : v4u{0u, 0u, 0u, 0u};
     }
-    if constexpr (GROUPED) {
-      // this lane holds C[channel 4*(lane/16)+r][token f*16 + lane%16]
-      if constexpr (OUT_I32) {
-        int32_t *o = (int32_t *)out + (int64_t)u * M * N;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const int t = f * 16 + (lane & 15);
+    for (int b = 0; b < BATCH; ++b) {
+      const int i = i0 + b;
+      if (i >= my_pieces) break;
+      v4i wop[KS], aop[4][KS];
+      if constexpr (CB == 4) {
+        widen16(wv[b], wop[0], wop[1]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int ch = n0 + 4 * (lane >> 4) + r;
-            if (t < M && ch < N) o[(int64_t)t * N + ch] = uacc[f][r] >> SHIFT;
-          }
-        }
+        for (int f = 0; f < 4; ++f) widen16(av[b][f], aop[f][0], aop[f][1]);
       } else {
+        wop[0] = __builtin_bit_cast(v4i, wv[b]);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) aop[f][0] = __builtin_bit_cast(v4i, av[b][f]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const int t = f * 16 + (lane & 15);
-          const float sav = t < M ? sa[(int64_t)t * G + u] * UNSCALE : 0.f;
+          if (GROUPED)
+            uacc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop[ks], aop[f][ks], uacc[f], 0, 0, 0);
+          else
+            acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop[ks], aop[f][ks], acc[f], 0, 0, 0);
+        }
+      if constexpr (GROUPED) {
+        if (i % ppu == ppu - 1) {   // unit (K-group) u complete
+          const int u = wave + kWaves * (i / ppu);
+          // this lane holds C[channel 4*(lane/16)+r][token f*16 + lane%16]
+          if constexpr (OUT_I32) {
+            int32_t *o = (int32_t *)out + (int64_t)u * M * N;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int ch = n0 + 4 * (lane >> 4) + r;
-            const float swv = ch < N ? sw[(int64_t)ch * G + u] : 0.f;
-            facc[f][r] = __builtin_fmaf((float)uacc[f][r], sav * swv, facc[f][r]);
+            for (int f = 0; f < 4; ++f) {
+              const int t = f * 16 + (lane & 15);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int ch = n0 + 4 * (lane >> 4) + r;
+                if (t < M && ch < N) o[(int64_t)t * N + ch] = uacc[f][r] >> SHIFT;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+              const int t = f * 16 + (lane & 15);
+              const float sav = t < M ? sa[(int64_t)t * G + u] * UNSCALE : 0.f;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int ch = n0 + 4 * (lane >> 4) + r;
+                const float swv = ch < N ? sw[(int64_t)ch * G + u] : 0.f;
+                facc[f][r] = __builtin_fmaf((float)uacc[f][r], sav * swv, facc[f][r]);
+              }
+            }
           }
+#pragma unroll
+          for (int f = 0; f < 4; ++f) uacc[f] = v4i{};
         }
       }
     }
