@@ -217,15 +217,15 @@ hipError_t launch_kv(const void *kv, int64_t T, int64_t H, int64_t ld_kv, const 
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   // persistent grid: as many blocks as are resident at once, each wave
   // walking its tiles with the next two in flight
-  static int per_cu = 0;
-  if (per_cu == 0) {
+  // resident blocks per CU: a constant of the kernel, queried once (a
+  // function-local static is initialised exactly once, thread-safely)
+  static const int per_cu = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kv_quant_kernel<SIGNS>, 64 * kWavesPerBlock, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kv_quant_kernel<SIGNS>, 64 * kWavesPerBlock, 0) != hipSuccess ||
         b < 1)
       b = 1;
-    per_cu = b;
-  }
+    return b;
+  }();
   const int64_t tiles = (T * H + 15) / 16;
   const int64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
   const int64_t cap = (int64_t)cus * per_cu;

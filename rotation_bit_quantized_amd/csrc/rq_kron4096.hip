@@ -304,14 +304,15 @@ hipError_t launch_m(const void *x, const void *up, int64_t rows, int64_t ld_x, c
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  static int per_cu = 0;
-  if (per_cu == 0) {
+  // resident blocks per CU: a constant of the kernel, queried once (a
+  // function-local static is initialised exactly once, thread-safely)
+  static const int per_cu = [] {
     int b = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rq_kron4096_kernel<M, FUSED>, 64 * kWaves, 0) != hipSuccess ||
         b < 1)
       b = 1;
-    per_cu = b;
-  }
+    return b;
+  }();
   const int64_t cap = (int64_t)cus * per_cu;
   const int64_t grid = rows < cap ? rows : cap;
   const float scale_mul = (float)(1.0 / (7.0 * 64.0));   // 1/(7 sqrt(4096))

@@ -406,15 +406,15 @@ hipError_t launch_one(const void *x, int64_t rows, int64_t ld_x, const int8_t *s
   int cus = 256;
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   // persistent grid: as many blocks as are resident at once
-  static int per_cu = 0;
-  if (per_cu == 0) {
+  // resident blocks per CU: a constant of the kernel, queried once (a
+  // function-local static is initialised exactly once, thread-safely)
+  static const int per_cu = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rq_pow2_kernel<L, GROUP, BITS>, 64 * waves_of<L>(), 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rq_pow2_kernel<L, GROUP, BITS>, 64 * waves_of<L>(), 0) != hipSuccess ||
         b < 1)
       b = 1;
-    per_cu = b;
-  }
+    return b;
+  }();
   constexpr int kWaves = waves_of<L>();
   const int64_t blocks_needed = (rows + kWaves - 1) / kWaves;
   const int64_t cap = (int64_t)cus * per_cu;
