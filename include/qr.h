@@ -231,8 +231,9 @@ qr_status qr_kv_quant(const void *kv_f16, int64_t T, int64_t H, int64_t head_dim
  *           sequence instead (no workspace; fewer blocks for small batches).
  *           A non-NULL workspace smaller than required gives QR_EINVAL.
  * out_f16   device fp16 [B][Hq][128] (2-byte aligned).
- * Hq % Hkv == 0; head_dim == 128.  The caller owns every buffer; concurrent
- * calls must not share a workspace.
+ * Hq % Hkv == 0; head_dim == 128; T * Hkv * 64 < 2^31 (one sequence's
+ * codes).  The caller owns every buffer; concurrent calls must not share a
+ * workspace.
  */
 qr_status qr_kv_attn_decode(const void *q_f16, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
                             int64_t head_dim, const uint8_t *k_codes, const float *k_scales,

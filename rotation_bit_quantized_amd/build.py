@@ -34,6 +34,9 @@ CFLAGS = [
 # AGPRs.
 EXTRA_FLAGS = {
     "rq_kron.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # the grouped-head attention rescales and stages its MFMA accumulators
+    # with VALU work: keep them in VGPRs (no AGPR copies every step)
+    "kv_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -219,6 +219,7 @@ qr_status qr_kv_attn_decode(const void *q_f16, int64_t B, int64_t Hq, int64_t Hk
   if (head_dim != 128) return QR_ESHAPE;
   if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return QR_ESHAPE;
   if (B > 65535 || Hq > 65535 || T > ((int64_t)1 << 30) || B * T * Hkv > ((int64_t)1 << 40)) return QR_ESHAPE;
+  if (T * Hkv * 64 >= ((int64_t)1 << 31)) return QR_ESHAPE;   // one sequence's cache rows: 32-bit byte offsets
   if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return QR_EINVAL;
   if (workspace_bytes < 0) return QR_EINVAL;
   if (B == 0 || Hq == 0) return QR_OK;
@@ -236,8 +237,8 @@ qr_status qr_kv_attn_decode(const void *q_f16, int64_t B, int64_t Hq, int64_t Hk
       // no workspace: one chunk per sequence
       plan.chunk = (T + 15) / 16 * 16;
       plan.splits = 1;
-      plan.tiles = B * plan.nhg;
-      plan.blocks = (plan.tiles + 7) / 8 * 8 * (Hq / Hkv);
+      plan.tiles = plan.gqa ? B * Hkv : B * plan.nhg;
+      plan.blocks = plan.gqa ? plan.tiles : (plan.tiles + 7) / 8 * 8 * (Hq / Hkv);
       plan.workspace_bytes = 0;
     } else if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
       return QR_EINVAL;

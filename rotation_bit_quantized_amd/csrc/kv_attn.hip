@@ -329,6 +329,268 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped query heads (Hq / Hkv = G in 4..16, e.g. LLaMA-2-70B's 64 / 8): one
+// block per (sequence, KV head, chunk) serves all G query heads on the matrix
+// cores, so every cache row is read and unpacked once.  Per 16-token step of
+// a wave (lane c16 = token for the A operands):
+//  * scores S^T[token][head] = K Q'^T on v_mfma_f32_16x16x32_f16: A = the key
+//    codes (a lane's 16 contiguous code bytes of its token; k-step s takes
+//    word s, its nibbles as exact fp16 via 0x6400 | n minus 1024), B = q'
+//    (fp16 high and low parts) in the same dim order: k = 8 kg + j <-> dim
+//    32 kg + 8 s + perm[j], perm = 0 4 1 5 2 6 3 7.  The output holds four
+//    consecutive tokens of one head per lane.
+//  * the value tile turned into dims x tokens by an MFMA against 0/1
+//    selection matrices (A = the value codes as 1024 + n, exact; output 16
+//    dims per tile), which also leaves four consecutive tokens per lane;
+//  * O^T += V^T P'^T on v_mfma_f32_16x16x16_f16 (P' = p D for the value
+//    steps, fp16 high and low parts): both operand layouts (four consecutive
+//    k per lane) are exactly the two outputs above.
+// Online softmax per head (lane column), merged over lanes and waves as in
+// the per-head kernel; partials and outputs in the same formats.
+constexpr int kGqaMaxG = 16;
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v8h codes_f16(unsigned w, unsigned magic, bool minus1024) {
+  v8h a;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    h2 e = __builtin_bit_cast(h2, ((w >> (4 * k)) & 0x000F000Fu) | magic);
+    if (minus1024) e = e - h2{(_Float16)1024.0f, (_Float16)1024.0f};   // exact: n
+    a[2 * k] = e[0];
+    a[2 * k + 1] = e[1];
+  }
+  return a;
+}
+
+__global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a) {
+  __shared__ float qbuf[kGqaMaxG * kD];
+  __shared__ float ostage[kWaves][kD][kGqaMaxG + 1];
+  __shared__ float wml[kWaves][2][kGqaMaxG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int G = a.G;
+
+  const int64_t u = blockIdx.x;
+  const int s = (int)(u % a.splits);
+  const int64_t bh = u / a.splits;
+  const int hk = (int)(bh % a.Hkv);
+  const int b = (int)(bh / a.Hkv);
+
+  int len = a.lens != nullptr ? a.lens[b] : a.T;
+  len = len < 0 ? 0 : (len > a.T ? a.T : len);
+  const int t0 = s * a.chunk;
+  const int t1 = t0 + a.chunk < len ? t0 + a.chunk : len;
+  const int nsteps = t1 > t0 ? (t1 - t0 + 15) / 16 : 0;
+
+  // ---- loads of one 16-token step (issued one step ahead).  The sequence's
+  // rows of this KV head start at uniform base pointers; a lane addresses
+  // its rows with 32-bit offsets (the host checks T * Hkv * 64 < 2^31).
+  const int64_t seq_row = (int64_t)b * a.T * a.Hkv + hk;
+  const uint8_t *const kc_b = a.kc + seq_row * 64;
+  const uint8_t *const vc_b = a.vc + seq_row * 64;
+  const float *const ks_b = a.ks + seq_row;
+  const float *const vs_b = a.vs + seq_row;
+  const uint8_t *const kz_b = a.kz + seq_row;
+  const uint8_t *const vz_b = a.vz + seq_row;
+  const unsigned hkv = (unsigned)a.Hkv;
+  struct Step {
+    v4u kc, vc;                  // this lane's token (c16): code words 4 g4 .. 4 g4 + 3
+    float kd[4], kz[4], vd[4], vz[4];   // the four tokens 4 g4 + r of the output layout
+    bool ok[4];
+  };
+  auto load = [&](int j, Step &st) __attribute__((always_inline)) {
+    const int base = t0 + 16 * j;
+    const int ta = base + c16;
+    const unsigned ra = (unsigned)(ta < t1 ? ta : t0) * hkv;
+    st.kc = *(const v4u *)(kc_b + (ra * 64u + 16u * (unsigned)g4));
+    st.vc = *(const v4u *)(vc_b + (ra * 64u + 16u * (unsigned)g4));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tc = base + 4 * g4 + r;
+      st.ok[r] = tc < t1;
+      const unsigned rc = (unsigned)(st.ok[r] ? tc : t0) * hkv;
+      st.kd[r] = *(const float *)((const uint8_t *)ks_b + rc * 4u);
+      st.kz[r] = (float)kz_b[rc];
+      st.vd[r] = *(const float *)((const uint8_t *)vs_b + rc * 4u);
+      st.vz[r] = (float)vz_b[rc];
+    }
+  };
+  Step sa, sb;
+  int j = wave;
+  if (j < nsteps) load(j, sa);   // in flight while the queries are prepared
+
+  // ---- q' for the G query heads of this KV head, as fp16 high / low B operands
+  for (int p = tid; p < G * kD; p += 64 * kWaves) {
+    const int r = p >> 7, d = p & 127;
+    float v = half_to_float(a.q[((int64_t)b * a.Hq + (int64_t)hk * G + r) * kD + d]);
+    if (a.signs != nullptr && a.signs[d] < 0) v = -v;
+    qbuf[p] = v;
+  }
+  wht128_rows(qbuf, G);
+  constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+  v8h qb[4][2];
+  float qsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int d = 32 * g4 + 8 * ks + kPerm[jj];
+      const float v = c16 < G ? qbuf[c16 * kD + d] * a.qmul : 0.f;
+      const _Float16 hi = (_Float16)v;
+      qb[ks][0][jj] = hi;
+      qb[ks][1][jj] = (_Float16)(v - (float)hi);
+      qsum += v;
+    }
+  qsum += __shfl_xor(qsum, 16);
+  qsum += __shfl_xor(qsum, 32);   // sum of q' over all 128 dims of head c16
+  // 0/1 selection B operands: output column n <- k = 8 (n >> 3) + (n & 7) of
+  // the lower (kg < 2) or upper (kg >= 2) half of the k-step
+  v8h selA, selB;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    selA[jj] = (g4 < 2 && c16 == 8 * g4 + jj) ? (_Float16)1.0f : (_Float16)0.0f;
+    selB[jj] = (g4 >= 2 && c16 == 8 * (g4 - 2) + jj) ? (_Float16)1.0f : (_Float16)0.0f;
+  }
+  unsigned magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));
+
+  float m = -__builtin_inff(), l = 0.f, zacc = 0.f;
+  v4f o[8];   // O^T tiles (k-step s, half h) -> o[2 s + h]: dims x heads
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](const Step &cur) __attribute__((always_inline)) {
+    // scores
+    v4f sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const v8h ak = codes_f16(cur.kc[ks], magic, true);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qb[ks][0], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qb[ks][1], sc, 0, 0, 0);
+    }
+    float smax = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = cur.ok[r] ? cur.kd[r] * (sc[r] - cur.kz[r] * qsum) : -__builtin_inff();
+      smax = fmaxf(smax, sc[r]);
+    }
+    {
+      float x0 = smax, x1 = smax;
+      swap16(x0, x1);
+      smax = fmaxf(x0, x1);
+      x0 = smax;
+      x1 = smax;
+      swap32(x0, x1);
+      smax = fmaxf(x0, x1);   // over the four lane groups: the head's step max
+    }
+    const float m_new = fmaxf(m, smax);
+    const float m_ref = m_new == -__builtin_inff() ? 0.f : m_new;
+    if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
+      l *= alpha;
+      zacc *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+    }
+    m = m_new;
+    v4h phi, plo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = __builtin_amdgcn_exp2f(sc[r] - m_ref);
+      l += p;
+      const float pv = p * cur.vd[r];
+      zacc = __builtin_fmaf(pv, cur.vz[r], zacc);
+      phi[r] = (_Float16)pv;
+      plo[r] = (_Float16)(pv - (float)phi[r]);
+    }
+    // values: dims x tokens tiles, then O^T += V^T P'^T
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const v8h av = codes_f16(cur.vc[ks], magic, false);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v4f t = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, h ? selB : selA, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        v4h vt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vt[r] = (_Float16)(t[r] - 1024.0f);   // exact small integers
+        o[2 * ks + h] = __builtin_amdgcn_mfma_f32_16x16x16f16(vt, phi, o[2 * ks + h], 0, 0, 0);
+        o[2 * ks + h] = __builtin_amdgcn_mfma_f32_16x16x16f16(vt, plo, o[2 * ks + h], 0, 0, 0);
+      }
+    }
+  };
+  // ping-pong over the two step buffers, each loaded one step ahead
+  while (j < nsteps) {
+    if (j + kWaves < nsteps) load(j + kWaves, sb);
+    step(sa);
+    j += kWaves;
+    if (j >= nsteps) break;
+    if (j + kWaves < nsteps) load(j + kWaves, sa);
+    step(sb);
+    j += kWaves;
+  }
+
+  // ---- per wave: l and the zero-point sum over the lane groups, stage O^T
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  zacc += __shfl_xor(zacc, 16);
+  zacc += __shfl_xor(zacc, 32);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mrow = 4 * g4 + r;   // output column of the selection = row of O^T
+        const int d = 32 * ((mrow >> 3) + 2 * h) + 8 * ks + kPerm[mrow & 7];
+        ostage[wave][d][c16] = o[2 * ks + h][r] - zacc;
+      }
+  if (g4 == 0) {
+    wml[wave][0][c16] = m;
+    wml[wave][1][c16] = l;
+  }
+  __syncthreads();
+
+  // ---- merge the waves per (head, dim)
+  for (int p = tid; p < G * kD; p += 64 * kWaves) {
+    const int hh = p >> 7, d = p & 127;
+    float mb = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mb = fmaxf(mb, wml[w][0][hh]);
+    const float mref = mb == -__builtin_inff() ? 0.f : mb;
+    float lb = 0.f, ob = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(wml[w][0][hh] - mref);
+      lb += f * wml[w][1][hh];
+      ob += f * ostage[w][d][hh];
+    }
+    const int hq = hk * G + hh;
+    if (a.splits == 1) {
+      qbuf[p] = lb > 0.f ? ob / lb : 0.f;
+    } else {
+      float *part = a.ws + (((int64_t)b * a.Hq + hq) * a.splits + s) * kPart;
+      part[4 + d] = ob;
+      if (d == 0) {
+        part[0] = mb;
+        part[1] = lb;
+      }
+    }
+  }
+  if (a.splits == 1) {
+    wht128_rows(qbuf, G);
+    for (int p = tid; p < G * kD; p += 64 * kWaves) {
+      const int hh = p >> 7, d = p & 127;
+      float v = qbuf[p] * 0.08838834764831845f;
+      if (a.signs != nullptr && a.signs[d] < 0) v = -v;
+      a.out[((int64_t)b * a.Hq + (int64_t)hk * G + hh) * kD + d] = float_to_half(v);
+    }
+  }
+}
+
 constexpr int kMaxSplits = 2048;   // the plan never splits a sequence further
 
 // Merge the chunks of one (sequence, query head): block-wide max of the
@@ -389,7 +651,8 @@ AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t T) {
   AttnPlan p{};
   const int64_t nhg = Hkv > 0 ? (Hkv + kHG - 1) / kHG : 0;
   const int64_t G = Hkv > 0 ? Hq / Hkv : 0;
-  const int64_t base = B * nhg * G;                              // blocks without splitting
+  p.gqa = G >= 4 && G <= kGqaMaxG;                               // all query heads of a KV head per block
+  const int64_t base = p.gqa ? B * Hkv : B * nhg * G;            // blocks without splitting
   int64_t splits = 1;
   if (T > 64 && base > 0) {
     const int64_t want = (1024 + base - 1) / base;               // about four blocks per CU of 256;
@@ -404,8 +667,8 @@ AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t T) {
   p.splits = (T + chunk - 1) / chunk;
   if (p.splits < 1) p.splits = 1;
   p.nhg = nhg;
-  p.tiles = B * nhg * p.splits;
-  p.blocks = (p.tiles + 7) / 8 * 8 * G;
+  p.tiles = p.gqa ? B * Hkv * p.splits : B * nhg * p.splits;
+  p.blocks = p.gqa ? p.tiles : (p.tiles + 7) / 8 * 8 * G;
   p.workspace_bytes = p.splits > 1 ? B * Hq * p.splits * kPart * (int64_t)sizeof(float) : 0;
   return p;
 }
@@ -435,7 +698,10 @@ hipError_t launch_attn_decode(const void *q, int64_t B, int64_t Hq, int64_t Hkv,
   a.splits = (int)plan.splits;
   a.ws = ws;
   a.out = (unsigned short *)out;
-  attn_decode_kernel<<<dim3((unsigned)plan.blocks), dim3(64 * kWaves), 0, stream>>>(a);
+  if (plan.gqa)
+    attn_decode_gqa_kernel<<<dim3((unsigned)plan.blocks), dim3(64 * kWaves), 0, stream>>>(a);
+  else
+    attn_decode_kernel<<<dim3((unsigned)plan.blocks), dim3(64 * kWaves), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
   attn_combine_kernel<<<dim3((unsigned)Hq, (unsigned)B), dim3(256), 0, stream>>>(a);

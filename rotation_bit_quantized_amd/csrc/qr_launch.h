@@ -74,6 +74,7 @@ struct AttnPlan {
   int64_t tiles;            // B * nhg * splits
   int64_t blocks;           // grid size
   int64_t workspace_bytes;
+  bool gqa;                 // 4..16 query heads per KV head: one block serves them all (MFMA kernel)
 };
 AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t T);
 hipError_t launch_attn_decode(const void *q, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, const uint8_t *kc,

@@ -93,3 +93,30 @@ def test_attn_full_size_sampled(qr):
     for b in (0, 37, 63):
         sub = tuple(a[b:b + 1] for a in cache)
         check_attn(got[b:b + 1], oracle(q[b:b + 1], sub), what=f"sequence {b}")
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,lens", [(2, 300, 16, 4, None), (3, 130, 32, 2, [0, 1, 129]),
+                                             (1, 1000, 16, 1, None), (2, 64, 40, 5, None)])
+def test_attn_grouped_heads(qr, B, T, Hq, Hkv, lens):
+    """4 to 16 query heads per KV head (the MFMA kernel that serves a KV
+    head's query heads together): split and unsplit, ragged and empty
+    sequences, a single KV head, a head count that is not a power of two."""
+    cache = W.make_attn_cache(B, T, Hkv, seed=T + Hq)
+    q = W.make_attn_query(B, Hq, seed=Hq + Hkv)
+    signs = np.where(np.random.default_rng(B).random(128) < 0.5, -1, 1).astype(np.int8)
+    ln = None if lens is None else np.array(lens, np.int32)
+    want = oracle(q, cache, lens=ln, signs=signs)
+    check_attn(run(qr, q, cache, lens=ln, signs=signs), want)
+    check_attn(run(qr, q, cache, lens=ln, signs=signs, workspace=False), want)
+
+
+def test_attn_grouped_full_size_sampled(qr):
+    """LLaMA-2-70B decode shape: 64 sequences x 2048 tokens, 64 query heads
+    over 8 KV heads; three sequences checked against the oracle."""
+    B, T, Hq, Hkv = 64, 2048, 64, 8
+    cache = W.make_attn_cache(B, T, Hkv, seed=8)
+    q = W.make_attn_query(B, Hq, seed=9)
+    got = run(qr, q, cache)
+    for b in (0, 31, 63):
+        sub = tuple(a[b:b + 1] for a in cache)
+        check_attn(got[b:b + 1], oracle(q[b:b + 1], sub), what=f"sequence {b}")
