@@ -170,6 +170,8 @@ def _attn(lib, **a):
     (dict(ws=None, wsb=1 << 20), qr.QR_EINVAL),  # a size without a buffer
     (dict(ws=MIS, wsb=1 << 30), qr.QR_EALIGN),
     (dict(wsb=-1), qr.QR_EINVAL),
+    (dict(T=1 << 25, Hq=1, Hkv=1), qr.QR_ESHAPE),   # one sequence's codes past 2^31 bytes
+    (dict(T=1 << 21), qr.QR_ESHAPE),
 ])
 def test_attn_rejects(args, expect):
     assert _attn(qr.library(), **args) == expect
