@@ -187,18 +187,6 @@ __global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
           }
     }
     __syncthreads();
-  } else {
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          smask[m][s][h][0] = smask[m][s][h][1] = 0u;
-          if (have_signs)
-            sign_masks4(*(const unsigned *)(signs + 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m),
-                        smask[m][s][h][0], smask[m][s][h][1]);
-        }
   }
   if (wave_id >= rows) return;
 
@@ -216,10 +204,35 @@ __global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
                                        (lds_void *)(bufs + b * ROWB + 1024 * i), 16, 0, 0);
   };
 
+  // Register sign masks: the sign words are loaded as one batch, and the
+  // first rows' DMA goes out before the masks wait for them.
+  unsigned sword[SIGNS_LDS ? 1 : MT][2][2];
+  if constexpr (!SIGNS_LDS) {
+    if (have_signs) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            sword[m][s][h] = *(const unsigned *)(signs + 4 * c16 + 64 * g + 256 * h + 512 * s + 1024 * m);
+    }
+  }
+
   issue_row(wave_id, 0);
   if constexpr (kBufs == 2) issue_row(wave_id + wave_stride, 1);
 
-  wait_vm<0>();   // the sign words (and the first rows) are in: no wait on them inside the loop
+  if constexpr (!SIGNS_LDS) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          smask[m][s][h][0] = smask[m][s][h][1] = 0u;
+          if (have_signs) sign_masks4(sword[m][s][h], smask[m][s][h][0], smask[m][s][h][1]);
+        }
+  }
 
   int it = 0;
   for (int64_t row = wave_id; row < rows; row += wave_stride, ++it) {
@@ -228,12 +241,14 @@ __global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
     // the following row (always), the stores of the previous row (it >= 1)
     // and of the one before, with the DMA of this row's follower in between
     // (it >= 2).  One buffer: only the previous row's stores (it >= 1).
+    // The sign words, where loaded, went out before the first row's DMA.
     if constexpr (kBufs == 2) {
       if (it == 0) wait_vm<DMA>();
       else if (it == 1) wait_vm<DMA + STORES>();
       else wait_vm<DMA + 2 * STORES>();
     } else {
       if (it > 0) wait_vm<STORES>();
+      else wait_vm<0>();
     }
 
     // ---- pass 1: 64-point factor on MFMA, A read from the LDS row buffer
