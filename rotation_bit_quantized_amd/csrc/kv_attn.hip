@@ -336,32 +336,34 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
 // a wave (lane c16 = token for the A operands):
 //  * scores S^T[token][head] = K Q'^T on v_mfma_f32_16x16x32_f16: A = the key
 //    codes (a lane's 16 contiguous code bytes of its token; k-step s takes
-//    word s, its nibbles as exact fp16 via 0x6400 | n minus 1024), B = q'
-//    (fp16 high and low parts) in the same dim order: k = 8 kg + j <-> dim
-//    32 kg + 8 s + perm[j], perm = 0 4 1 5 2 6 3 7.  The output holds four
-//    consecutive tokens of one head per lane.
-//  * the value tile turned into dims x tokens by an MFMA against 0/1
-//    selection matrices (A = the value codes as 1024 + n, exact; output 16
-//    dims per tile), which also leaves four consecutive tokens per lane;
+//    word s), B = q' (fp16 high and low parts) in the same dim order: k =
+//    8 kg + j <-> dim 32 kg + 8 s + perm[j], perm = 0 4 1 5 2 6 3 7.  A code
+//    nibble enters as the fp16 bit pattern it forms in place, masked: the
+//    subnormal n 2^-24 (perm slots 0, 1, 4, 5) or 16 n 2^-24 (slots 2, 3,
+//    6, 7, whose B entries carry 1/16), all exact, one AND per two codes.
+//    The output holds four consecutive tokens of one head per lane, in units
+//    of 2^-24.
+//  * the value tile turned into dims x tokens by an MFMA against selection
+//    matrices (A = the value codes as above, B = 1 or 1/16; the output n
+//    2^-24 is exact in fp16 as well; 16 dims per tile), which also leaves
+//    four consecutive tokens per lane;
 //  * O^T += V^T P'^T on v_mfma_f32_16x16x16_f16 (P' = p D for the value
-//    steps, fp16 high and low parts): both operand layouts (four consecutive
-//    k per lane) are exactly the two outputs above.
+//    steps, fp16 high and low parts; O^T in units of 2^-24): both operand
+//    layouts (four consecutive k per lane) are exactly the two outputs above.
 // Online softmax per head (lane column), merged over lanes and waves as in
 // the per-head kernel; partials and outputs in the same formats.
 constexpr int kGqaMaxG = 16;
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ v8h codes_f16(unsigned w, unsigned magic, bool minus1024) {
-  v8h a;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    h2 e = __builtin_bit_cast(h2, ((w >> (4 * k)) & 0x000F000Fu) | magic);
-    if (minus1024) e = e - h2{(_Float16)1024.0f, (_Float16)1024.0f};   // exact: n
-    a[2 * k] = e[0];
-    a[2 * k + 1] = e[1];
-  }
-  return a;
+// The eight nibbles of a code word as fp16 subnormals, in perm order:
+// slots (0, 1) = nibbles (0, 4) as n 2^-24, (2, 3) = nibbles (1, 5) as
+// 16 n 2^-24, (4, 5) = nibbles (2, 6), (6, 7) = nibbles (3, 7) likewise.
+__device__ __forceinline__ v8h codes_sub(unsigned w) {
+  const unsigned w8 = w >> 8;
+  return __builtin_bit_cast(v8h, v4u{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u});
 }
+// scale of perm slot j in codes_sub, inverted
+__device__ __forceinline__ constexpr float slot_unscale(int j) { return (j & 2) ? 0.0625f : 1.0f; }
 
 __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a) {
   __shared__ float qbuf[kGqaMaxG * kD];
@@ -440,23 +442,25 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
     for (int jj = 0; jj < 8; ++jj) {
       const int d = 32 * g4 + 8 * ks + kPerm[jj];
       const float v = c16 < G ? qbuf[c16 * kD + d] * a.qmul : 0.f;
-      const _Float16 hi = (_Float16)v;
+      const float vs = v * slot_unscale(jj);   // exact: a power of two
+      const _Float16 hi = (_Float16)vs;
       qb[ks][0][jj] = hi;
-      qb[ks][1][jj] = (_Float16)(v - (float)hi);
+      qb[ks][1][jj] = (_Float16)(vs - (float)hi);
       qsum += v;
     }
   qsum += __shfl_xor(qsum, 16);
   qsum += __shfl_xor(qsum, 32);   // sum of q' over all 128 dims of head c16
-  // 0/1 selection B operands: output column n <- k = 8 (n >> 3) + (n & 7) of
-  // the lower (kg < 2) or upper (kg >= 2) half of the k-step
+  const float qsum24 = qsum * 0x1p-24f;   // in the scores' units
+  // selection B operands: output column n <- k = 8 (n >> 3) + (n & 7) of
+  // the lower (kg < 2) or upper (kg >= 2) half of the k-step, weighted by the
+  // slot's unscale so that every output is n 2^-24
   v8h selA, selB;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    selA[jj] = (g4 < 2 && c16 == 8 * g4 + jj) ? (_Float16)1.0f : (_Float16)0.0f;
-    selB[jj] = (g4 >= 2 && c16 == 8 * (g4 - 2) + jj) ? (_Float16)1.0f : (_Float16)0.0f;
+    const _Float16 one = (_Float16)slot_unscale(jj);
+    selA[jj] = (g4 < 2 && c16 == 8 * g4 + jj) ? one : (_Float16)0.0f;
+    selB[jj] = (g4 >= 2 && c16 == 8 * (g4 - 2) + jj) ? one : (_Float16)0.0f;
   }
-  unsigned magic = 0x64006400u;
-  asm volatile("" : "+v"(magic));
 
   float m = -__builtin_inff(), l = 0.f, zacc = 0.f;
   v4f o[8];   // O^T tiles (k-step s, half h) -> o[2 s + h]: dims x heads
@@ -468,14 +472,14 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
     v4f sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const v8h ak = codes_f16(cur.kc[ks], magic, true);
+      const v8h ak = codes_sub(cur.kc[ks]);
       sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qb[ks][0], sc, 0, 0, 0);
       sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qb[ks][1], sc, 0, 0, 0);
     }
     float smax = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sc[r] = cur.ok[r] ? cur.kd[r] * (sc[r] - cur.kz[r] * qsum) : -__builtin_inff();
+      sc[r] = cur.ok[r] ? cur.kd[r] * (sc[r] - cur.kz[r] * qsum24) : -__builtin_inff();   // score 2^-24
       smax = fmaxf(smax, sc[r]);
     }
     {
@@ -485,7 +489,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
       x0 = smax;
       x1 = smax;
       swap32(x0, x1);
-      smax = fmaxf(x0, x1);   // over the four lane groups: the head's step max
+      smax = fmaxf(x0, x1) * 0x1p24f;   // over the four lane groups: the head's step max
     }
     const float m_new = fmaxf(m, smax);
     const float m_ref = m_new == -__builtin_inff() ? 0.f : m_new;
@@ -500,7 +504,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
     v4h phi, plo;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = __builtin_amdgcn_exp2f(sc[r] - m_ref);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], 0x1p24f, -m_ref));
       l += p;
       const float pv = p * cur.vd[r];
       zacc = __builtin_fmaf(pv, cur.vz[r], zacc);
@@ -510,13 +514,13 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
     // values: dims x tokens tiles, then O^T += V^T P'^T
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const v8h av = codes_f16(cur.vc[ks], magic, false);
+      const v8h av = codes_sub(cur.vc[ks]);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         v4f t = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, h ? selB : selA, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         v4h vt;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vt[r] = (_Float16)(t[r] - 1024.0f);   // exact small integers
+        for (int r = 0; r < 4; ++r) vt[r] = (_Float16)t[r];   // exact: n 2^-24
         o[2 * ks + h] = __builtin_amdgcn_mfma_f32_16x16x16f16(vt, phi, o[2 * ks + h], 0, 0, 0);
         o[2 * ks + h] = __builtin_amdgcn_mfma_f32_16x16x16f16(vt, plo, o[2 * ks + h], 0, 0, 0);
       }
@@ -546,7 +550,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
       for (int r = 0; r < 4; ++r) {
         const int mrow = 4 * g4 + r;   // output column of the selection = row of O^T
         const int d = 32 * ((mrow >> 3) + 2 * h) + 8 * ks + kPerm[mrow & 7];
-        ostage[wave][d][c16] = o[2 * ks + h][r] - zacc;
+        ostage[wave][d][c16] = __builtin_fmaf(o[2 * ks + h][r], 0x1p24f, -zacc);
       }
   if (g4 == 0) {
     wml[wave][0][c16] = m;
@@ -655,10 +659,23 @@ AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t T) {
   const int64_t base = p.gqa ? B * Hkv : B * nhg * G;            // blocks without splitting
   int64_t splits = 1;
   if (T > 64 && base > 0) {
-    const int64_t want = (1024 + base - 1) / base;               // about four blocks per CU of 256;
-                                                                 // at most kMaxSplits
-    const int64_t most = (T + 63) / 64;                          // chunks of at least 64 tokens
-    splits = want < most ? want : most;
+    // Both kernels run 4-wave blocks at 3 waves per SIMD: 768 resident blocks
+    // on 256 CUs.  A launch takes ceil(blocks / 768) rounds, each as long as
+    // one block: its chunk plus a fixed cost (query setup and merge, about
+    // 80 tokens' worth).  Take the split count with the least estimate,
+    // chunks of at least 64 tokens, at most kMaxSplits.
+    constexpr int64_t kResident = 768, kFixed = 80;
+    int64_t most = (T + 63) / 64;
+    most = most < kMaxSplits ? most : kMaxSplits;
+    int64_t best = -1;
+    for (int64_t sp = 1; sp <= most; ++sp) {
+      const int64_t ck = ((T + sp - 1) / sp + 15) / 16 * 16;
+      const int64_t est = ((base * sp + kResident - 1) / kResident) * (ck + kFixed);
+      if (best < 0 || est < best) {
+        best = est;
+        splits = sp;
+      }
+    }
   }
   int64_t chunk = (T + splits - 1) / splits;
   chunk = (chunk + 15) / 16 * 16;

@@ -183,15 +183,16 @@ def test_attn_empty_batch_is_noop():
 
 
 def test_attn_workspace_size():
-    """Blocks take up to eight KV heads; a shape with fewer than 1024 such
-    blocks is split into chunks of at least 64 tokens, each chunk leaving a
-    partial of 132 floats per query head.  One query per head over 4096
-    tokens: 4 head groups -> 64 chunks.  64 sequences x 2048 tokens: 256
-    head groups -> 4 chunks; with 8 query heads per KV head, 512 blocks ->
-    2 chunks.  64 tokens or fewer are never split."""
+    """A sequence is split into chunks of at least 64 tokens so that the
+    blocks fill whole rounds of the 768 that are resident at once; each
+    chunk leaves a partial of 132 floats per query head.  One query per head
+    over 4096 tokens: 4 blocks of eight KV heads -> 64 chunks.  64 sequences
+    x 2048 tokens, 32 heads: 256 blocks -> 3 chunks (one round of 768).
+    With 8 query heads per KV head: 512 (sequence, KV head) blocks -> 3
+    chunks (two rounds).  64 tokens or fewer are never split."""
     assert qr.kv_attn_decode_workspace(1, 32, 32, 4096) == 32 * 64 * 132 * 4
-    assert qr.kv_attn_decode_workspace(64, 32, 32, 2048) == 64 * 32 * 4 * 132 * 4
-    assert qr.kv_attn_decode_workspace(64, 64, 8, 2048) == 64 * 64 * 2 * 132 * 4
+    assert qr.kv_attn_decode_workspace(64, 32, 32, 2048) == 64 * 32 * 3 * 132 * 4
+    assert qr.kv_attn_decode_workspace(64, 64, 8, 2048) == 64 * 64 * 3 * 132 * 4
     assert qr.kv_attn_decode_workspace(4, 32, 32, 64) == 0
     with pytest.raises(qr.QRError):
         qr.kv_attn_decode_workspace(1, 32, 32, 4096, head_dim=64)
