@@ -381,7 +381,7 @@ def main():
         suite(args)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the hot path is per-token independent and would shard tokens across GPUs with no exchange).",
               file=sys.stderr)
         sys.exit(2)
