@@ -365,7 +365,7 @@ __device__ __forceinline__ v8h codes_sub(unsigned w) {
 // scale of perm slot j in codes_sub, inverted
 __device__ __forceinline__ constexpr float slot_unscale(int j) { return (j & 2) ? 0.0625f : 1.0f; }
 
-__global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 3) void attn_decode_gqa_kernel(AttnArgs a) {
   __shared__ float qbuf[kGqaMaxG * kD];
   __shared__ float ostage[kWaves][kD][kGqaMaxG + 1];
   __shared__ float wml[kWaves][2][kGqaMaxG];
@@ -399,10 +399,13 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
   const uint8_t *const kz_b = a.kz + seq_row;
   const uint8_t *const vz_b = a.vz + seq_row;
   const unsigned hkv = (unsigned)a.Hkv;
+  // A step's per-token scales and zero points: lane l loads one value, of
+  // token c16 (= l mod 16) from array g4 (k step, k zero, v step, v zero);
+  // the lanes that need it fetch it with ds_bpermute when the step runs.
+  // Small step buffers let three of them (two steps in flight) fit.
   struct Step {
-    v4u kc, vc;                  // this lane's token (c16): code words 4 g4 .. 4 g4 + 3
-    float kd[4], kz[4], vd[4], vz[4];   // the four tokens 4 g4 + r of the output layout
-    bool ok[4];
+    v4u kc, vc;   // this lane's token (c16): code words 4 g4 .. 4 g4 + 3
+    float meta;
   };
   auto load = [&](int j, Step &st) __attribute__((always_inline)) {
     const int base = t0 + 16 * j;
@@ -410,20 +413,13 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
     const unsigned ra = (unsigned)(ta < t1 ? ta : t0) * hkv;
     st.kc = *(const v4u *)(kc_b + (ra * 64u + 16u * (unsigned)g4));
     st.vc = *(const v4u *)(vc_b + (ra * 64u + 16u * (unsigned)g4));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tc = base + 4 * g4 + r;
-      st.ok[r] = tc < t1;
-      const unsigned rc = (unsigned)(st.ok[r] ? tc : t0) * hkv;
-      st.kd[r] = *(const float *)((const uint8_t *)ks_b + rc * 4u);
-      st.kz[r] = (float)kz_b[rc];
-      st.vd[r] = *(const float *)((const uint8_t *)vs_b + rc * 4u);
-      st.vz[r] = (float)vz_b[rc];
-    }
+    if (g4 & 1) st.meta = (float)((g4 & 2) ? vz_b : kz_b)[ra];
+    else st.meta = *(const float *)((const uint8_t *)((g4 & 2) ? vs_b : ks_b) + ra * 4u);
   };
-  Step sa, sb;
+  Step sa, sb, sc;
   int j = wave;
   if (j < nsteps) load(j, sa);   // in flight while the queries are prepared
+  if (j + kWaves < nsteps) load(j + kWaves, sb);
 
   // ---- q' for the G query heads of this KV head, as fp16 high / low B operands
   for (int p = tid; p < G * kD; p += 64 * kWaves) {
@@ -467,7 +463,20 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](const Step &cur) __attribute__((always_inline)) {
+  auto step = [&](const Step &cur, int jj) __attribute__((always_inline)) {
+    // this lane's four tokens 4 g4 + r: in range, and their scales and zero points
+    bool ok[4];
+    float kd[4], kz[4], vd[4], vz[4];
+    const int mi = __builtin_bit_cast(int, cur.meta);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ok[r] = t0 + 16 * jj + 4 * g4 + r < t1;
+      const int src = 4 * (4 * g4 + r);   // byte address of lane 4 g4 + r in the array-0 group
+      kd[r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, mi));
+      kz[r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src + 64, mi));
+      vd[r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src + 128, mi));
+      vz[r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src + 192, mi));
+    }
     // scores
     v4f sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -479,7 +488,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
     float smax = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sc[r] = cur.ok[r] ? cur.kd[r] * (sc[r] - cur.kz[r] * qsum24) : -__builtin_inff();   // score 2^-24
+      sc[r] = ok[r] ? kd[r] * (sc[r] - kz[r] * qsum24) : -__builtin_inff();   // score 2^-24
       smax = fmaxf(smax, sc[r]);
     }
     {
@@ -506,8 +515,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
     for (int r = 0; r < 4; ++r) {
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], 0x1p24f, -m_ref));
       l += p;
-      const float pv = p * cur.vd[r];
-      zacc = __builtin_fmaf(pv, cur.vz[r], zacc);
+      const float pv = p * vd[r];
+      zacc = __builtin_fmaf(pv, vz[r], zacc);
       phi[r] = (_Float16)pv;
       plo[r] = (_Float16)(pv - (float)phi[r]);
     }
@@ -526,14 +535,18 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_gqa_kernel(AttnArgs a
       }
     }
   };
-  // ping-pong over the two step buffers, each loaded one step ahead
+  // a ring of three step buffers, each loaded two steps ahead
   while (j < nsteps) {
-    if (j + kWaves < nsteps) load(j + kWaves, sb);
-    step(sa);
+    if (j + 2 * kWaves < nsteps) load(j + 2 * kWaves, sc);
+    step(sa, j);
     j += kWaves;
     if (j >= nsteps) break;
-    if (j + kWaves < nsteps) load(j + kWaves, sa);
-    step(sb);
+    if (j + 2 * kWaves < nsteps) load(j + 2 * kWaves, sa);
+    step(sb, j);
+    j += kWaves;
+    if (j >= nsteps) break;
+    if (j + 2 * kWaves < nsteps) load(j + 2 * kWaves, sb);
+    step(sc, j);
     j += kWaves;
   }
 
