@@ -108,6 +108,20 @@ def test_rq_c3_kron_rows(qr):
     check_rq(qr, x, c.K, had_n=64, dense=W.make_dense(c))
 
 
+def test_rq_c3_kron_measured_launch_sampled(qr):
+    """The 16384-row launch the kernel suite times (32 rows per block of the
+    two-blocks-per-CU grid): the first, a middle and the last rows against
+    the oracle."""
+    c = W.CONFIGS["c3"]
+    rows = 16384
+    x = W.make_x(c, rows=np.arange(rows))
+    codes, scales = gpu_rq(qr, x, c.K, had_n=64, dense=W.make_dense(c))
+    pick = np.r_[np.arange(64), np.arange(8190, 8230), np.arange(rows - 33, rows)]
+    q, s, t = oracle_rq(x[pick], c.K, had_n=64, dense=W.make_dense(c))
+    check_symmetric_codes(codes[pick], q, t)
+    check_scales(scales[pick], s)
+
+
 @pytest.mark.parametrize("n", [2, 8, 64, 256, 1024, 2048, 4096, 8192, 16384, 32768])
 @pytest.mark.parametrize("rows", [1, 3, 130])
 def test_rq_widths_and_ragged_rows(qr, n, rows):
@@ -166,7 +180,7 @@ def test_rq_kron_small_dense(qr):
 
 
 @pytest.mark.parametrize("m,rows", [(172, 5), (176, 64), (8, 33), (100, 130), (4, 3),
-                                    (8, 3000), (100, 1000), (172, 600)])
+                                    (8, 3000), (100, 1000), (172, 600), (172, 2600)])
 def test_rq_kron_fast_path(qr, m, rows):
     """64 x m Kronecker rotations without signs (the MFMA Kronecker kernel);
     the larger row counts give each persistent block several rows."""
