@@ -662,6 +662,55 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
+// Few chunks (at most kFewSplits): one wave per (sequence, query head), four
+// to a block.  A lane merges dims lane and lane + 64 over the chunks, and the
+// inverse 128-point transform runs in the wave's registers: the butterfly
+// over index bit 6 inside the lane, bits 0-5 by lane exchanges.  No LDS, no
+// barrier; the block-wide kernel above serves long split lists.
+constexpr int kFewSplits = 16;
+
+__global__ __launch_bounds__(256) void attn_combine_few_kernel(AttnArgs a, int64_t nheads) {
+  const int lane = threadIdx.x & 63;
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // b * Hq + hq
+  if (u >= nheads) return;
+  const int S = a.splits;
+  const float *part = a.ws + u * S * kPart;
+  float mb = -__builtin_inff();
+  for (int s = 0; s < S; ++s) mb = fmaxf(mb, part[s * kPart]);
+  const float mref = mb == -__builtin_inff() ? 0.f : mb;
+  float lb = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float *e = part + s * kPart;
+    const float f = __builtin_amdgcn_exp2f(e[0] - mref);
+    lb += f * e[1];
+    o0 += f * e[4 + lane];
+    o1 += f * e[4 + 64 + lane];
+  }
+  float v0 = lb > 0.f ? o0 / lb : 0.f;
+  float v1 = lb > 0.f ? o1 / lb : 0.f;
+  // out = o R^T: H_128 (Sylvester) over d = 64 h + lane
+  {
+    const float t0 = v0 + v1, t1 = v0 - v1;
+    v0 = t0;
+    v1 = t1;
+  }
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) {
+    const float p0 = __shfl_xor(v0, k), p1 = __shfl_xor(v1, k);
+    const bool hi = (lane & k) != 0;
+    v0 = hi ? p0 - v0 : v0 + p0;
+    v1 = hi ? p1 - v1 : v1 + p1;
+  }
+  unsigned short *out = a.out + u * kD;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int d = 64 * h + lane;
+    float v = (h ? v1 : v0) * 0.08838834764831845f;
+    if (a.signs != nullptr && a.signs[d] < 0) v = -v;
+    out[d] = float_to_half(v);
+  }
+}
+
 }  // namespace
 
 AttnPlan attn_decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t T) {
@@ -734,7 +783,12 @@ hipError_t launch_attn_decode(const void *q, int64_t B, int64_t Hq, int64_t Hkv,
     attn_decode_kernel<<<dim3((unsigned)plan.blocks), dim3(64 * kWaves), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  attn_combine_kernel<<<dim3((unsigned)Hq, (unsigned)B), dim3(256), 0, stream>>>(a);
+  if (plan.splits <= kFewSplits) {
+    const int64_t nheads = B * Hq;
+    attn_combine_few_kernel<<<dim3((unsigned)((nheads + 3) / 4)), dim3(256), 0, stream>>>(a, nheads);
+  } else {
+    attn_combine_kernel<<<dim3((unsigned)Hq, (unsigned)B), dim3(256), 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
