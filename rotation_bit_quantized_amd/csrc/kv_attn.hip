@@ -662,12 +662,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
-// Few chunks (at most kFewSplits): one wave per (sequence, query head), four
+// Few chunks (at most kFewSplits; the loops over them are unrolled by four so
+// that their loads overlap): one wave per (sequence, query head), four
 // to a block.  A lane merges dims lane and lane + 64 over the chunks, and the
 // inverse 128-point transform runs in the wave's registers: the butterfly
 // over index bit 6 inside the lane, bits 0-5 by lane exchanges.  No LDS, no
 // barrier; the block-wide kernel above serves long split lists.
-constexpr int kFewSplits = 16;
+constexpr int kFewSplits = 8;
 
 __global__ __launch_bounds__(256) void attn_combine_few_kernel(AttnArgs a, int64_t nheads) {
   const int lane = threadIdx.x & 63;
@@ -676,9 +677,11 @@ __global__ __launch_bounds__(256) void attn_combine_few_kernel(AttnArgs a, int64
   const int S = a.splits;
   const float *part = a.ws + u * S * kPart;
   float mb = -__builtin_inff();
+#pragma unroll 4
   for (int s = 0; s < S; ++s) mb = fmaxf(mb, part[s * kPart]);
   const float mref = mb == -__builtin_inff() ? 0.f : mb;
   float lb = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
   for (int s = 0; s < S; ++s) {
     const float *e = part + s * kPart;
     const float f = __builtin_amdgcn_exp2f(e[0] - mref);
