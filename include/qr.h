@@ -119,8 +119,10 @@ qr_status qr_rotate_quant(const void *x_f16, int64_t rows, int64_t ld_x,
  * a_scales  device, fp32 [M] or [M][K/group]
  * w_codes   device, [N][K/2] packed codes, one row per output channel
  * w_scales  device, fp32 [N] or [N][K/group]
- * M, N >= 0; K > 0, a multiple of 128 and at most 131072 (the int32 sums
- * stay exact); group 0 or a multiple of 128 that divides K.
+ * M, N >= 0; K > 0, a multiple of 128 and below 2^17, i.e. at most 130944
+ * (every product is at most 2^14 in magnitude, so the int32 sums stay
+ * exact; K >= 2^17 returns QR_ESHAPE); group 0 or a multiple of 128 that
+ * divides K.
  * y_f16     device, fp16 [M][ld_y], ld_y >= N, 2-byte aligned.
  *
  * M <= 64 runs the memory-bound decode kernel (weights streamed once); larger
@@ -167,7 +169,8 @@ qr_status qr_rotate_quant_i8(const void *x_f16, int64_t rows, int64_t ld_x,
  * The GEMM of qr_int4_gemm on int8 codes (the 6- and 8-bit variants): the
  * codes go into the int8 matrix cores as they are.  a_codes [M][K] and
  * w_codes [N][K] int8 (16-byte aligned); every other argument and the
- * epilogue as for qr_int4_gemm.  K <= 131072 keeps the int32 sums exact.
+ * epilogue as for qr_int4_gemm.  K < 2^17 (at most 130944) keeps the int32
+ * sums exact.
  */
 qr_status qr_int8_gemm(const int8_t *a_codes, const float *a_scales,
                        const int8_t *w_codes, const float *w_scales,

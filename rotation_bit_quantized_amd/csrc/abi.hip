@@ -27,14 +27,37 @@ qr_status check_rotation(const qr_rotation *rot) {
 
 qr_status check_gemm(const uint8_t *a, const uint8_t *w, int64_t M, int64_t N, int64_t K, int64_t group) {
   if (M < 0 || N < 0 || K <= 0) return QR_EINVAL;
-  // |product| <= 128 * 128 (8-bit codes, or 4-bit codes widened to 16 q):
-  // int32 sums stay exact for K <= 2^17
-  if (K % 128 != 0 || K > (int64_t)1 << 17) return QR_ESHAPE;
+  // |product| <= 128 * 128 = 2^14 (8-bit codes, or 4-bit codes widened to
+  // 16 q): int32 sums stay exact while K * 2^14 < 2^31, i.e. K < 2^17
+  // (largest valid K: 130944)
+  if (K % 128 != 0 || K >= (int64_t)1 << 17) return QR_ESHAPE;
   if (group != 0 && (group < 128 || group % 128 != 0 || K % group != 0)) return QR_ESHAPE;
   if (M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30)) return QR_ESHAPE;
   if (M == 0 || N == 0) return QR_OK;
   if (a == nullptr || w == nullptr) return QR_EINVAL;
   if (!aligned(a, 16) || !aligned(w, 16)) return QR_EALIGN;
+  return QR_OK;
+}
+
+qr_status check_attn(const void *q_f16, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t head_dim,
+                     const uint8_t *k_codes, const float *k_scales, const uint8_t *k_zeros, const uint8_t *v_codes,
+                     const float *v_scales, const uint8_t *v_zeros, const int32_t *lens, const int8_t *signs,
+                     float sm_scale, const void *out_f16) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || T < 0) return QR_EINVAL;
+  if (head_dim != 128) return QR_ESHAPE;
+  if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return QR_ESHAPE;
+  if (B > 65535 || Hq > 65535 || T > ((int64_t)1 << 30) || B * T * Hkv > ((int64_t)1 << 40)) return QR_ESHAPE;
+  if (T * Hkv * 64 >= ((int64_t)1 << 31)) return QR_ESHAPE;   // one sequence's cache rows: 32-bit byte offsets
+  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return QR_EINVAL;
+  if (B == 0 || Hq == 0) return QR_OK;
+  if (q_f16 == nullptr || out_f16 == nullptr) return QR_EINVAL;
+  if (T > 0 && (k_codes == nullptr || k_scales == nullptr || k_zeros == nullptr || v_codes == nullptr ||
+                v_scales == nullptr || v_zeros == nullptr))
+    return QR_EINVAL;
+  if (!aligned(q_f16, 2) || !aligned(out_f16, 2)) return QR_EALIGN;
+  if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
+    return QR_EALIGN;
+  if ((lens != nullptr && !aligned(lens, 4)) || (signs != nullptr && !aligned(signs, 4))) return QR_EALIGN;
   return QR_OK;
 }
 
@@ -215,22 +238,11 @@ qr_status qr_kv_attn_decode(const void *q_f16, int64_t B, int64_t Hq, int64_t Hk
                             const uint8_t *v_codes, const float *v_scales, const uint8_t *v_zeros,
                             const int32_t *lens, const int8_t *signs, float sm_scale, void *workspace,
                             int64_t workspace_bytes, void *out_f16, void *stream) {
-  if (B < 0 || Hq < 0 || Hkv < 0 || T < 0) return QR_EINVAL;
-  if (head_dim != 128) return QR_ESHAPE;
-  if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return QR_ESHAPE;
-  if (B > 65535 || Hq > 65535 || T > ((int64_t)1 << 30) || B * T * Hkv > ((int64_t)1 << 40)) return QR_ESHAPE;
-  if (T * Hkv * 64 >= ((int64_t)1 << 31)) return QR_ESHAPE;   // one sequence's cache rows: 32-bit byte offsets
-  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return QR_EINVAL;
+  qr_status st = check_attn(q_f16, B, Hq, Hkv, T, head_dim, k_codes, k_scales, k_zeros, v_codes, v_scales,
+                            v_zeros, lens, signs, sm_scale, out_f16);
+  if (st != QR_OK) return st;
   if (workspace_bytes < 0) return QR_EINVAL;
   if (B == 0 || Hq == 0) return QR_OK;
-  if (q_f16 == nullptr || out_f16 == nullptr) return QR_EINVAL;
-  if (T > 0 && (k_codes == nullptr || k_scales == nullptr || k_zeros == nullptr || v_codes == nullptr ||
-                v_scales == nullptr || v_zeros == nullptr))
-    return QR_EINVAL;
-  if (!aligned(q_f16, 2) || !aligned(out_f16, 2)) return QR_EALIGN;
-  if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
-    return QR_EALIGN;
-  if ((lens != nullptr && !aligned(lens, 4)) || (signs != nullptr && !aligned(signs, 4))) return QR_EALIGN;
   qr::AttnPlan plan = qr::attn_decode_plan(B, Hq, Hkv, T);
   if (plan.splits > 1) {
     if (workspace == nullptr && workspace_bytes == 0) {

@@ -28,20 +28,6 @@ namespace {
 constexpr int kWaves = 16;
 constexpr int kNT = 16;  // output channels per workgroup
 
-// 32 packed codes (16 bytes) -> two MFMA operands of 16 int8 values 16 q
-// (the high-nibble form of the prefill kernel; the k order inside a dword
-// is permuted identically on both sides).
-__device__ __forceinline__ void widen16(const v4u &w, v4i &op0, v4i &op1) {
-  op0[0] = (int)((w[0] << 4) & 0xF0F0F0F0u);
-  op0[1] = (int)(w[0] & 0xF0F0F0F0u);
-  op0[2] = (int)((w[1] << 4) & 0xF0F0F0F0u);
-  op0[3] = (int)(w[1] & 0xF0F0F0F0u);
-  op1[0] = (int)((w[2] << 4) & 0xF0F0F0F0u);
-  op1[1] = (int)(w[2] & 0xF0F0F0F0u);
-  op1[2] = (int)((w[3] << 4) & 0xF0F0F0F0u);
-  op1[3] = (int)(w[3] & 0xF0F0F0F0u);
-}
-
 template <bool GROUPED, bool OUT_I32, int CB = 4>
 __global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ W,
@@ -104,9 +90,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_kernel(
       if (i >= my_pieces) break;
       v4i wop[KS], aop[4][KS];
       if constexpr (CB == 4) {
-        widen16(wv[b], wop[0], wop[1]);
+        widen_hi_nibble(wv[b], wop[0], wop[1]);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) widen16(av[b][f], aop[f][0], aop[f][1]);
+        for (int f = 0; f < 4; ++f) widen_hi_nibble(av[b][f], aop[f][0], aop[f][1]);
       } else {
         wop[0] = __builtin_bit_cast(v4i, wv[b]);
 #pragma unroll

@@ -12,7 +12,8 @@
 // turns 8 packed codes into 8 int8 values 16*q (exact for q in [-8, 7]) in
 // three VALU ops.  A and W are widened identically, so the product sums
 // 256 * q_a * q_w; the k order inside a dword is permuted the same way on
-// both sides and cancels.  |acc| <= 64 * 256 * K < 2^31 for K <= 131072.
+// both sides and cancels.  |acc| <= 64 * 256 * K < 2^31 for K < 2^17 (the
+// host rejects larger K).
 // The 1/256 is an exact power of two folded into the epilogue (or a shift
 // for the int32 output).
 //
@@ -53,30 +54,10 @@ namespace {
 
 constexpr int kRowBytes = 128;   // bytes per row per K-tile (256 4-bit or 128 8-bit codes)
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void widen(const v4u &w, v4i &op0, v4i &op1) {
-  op0[0] = (int)((w[0] << 4) & 0xF0F0F0F0u);
-  op0[1] = (int)(w[0] & 0xF0F0F0F0u);
-  op0[2] = (int)((w[1] << 4) & 0xF0F0F0F0u);
-  op0[3] = (int)(w[1] & 0xF0F0F0F0u);
-  op1[0] = (int)((w[2] << 4) & 0xF0F0F0F0u);
-  op1[1] = (int)(w[2] & 0xF0F0F0F0u);
-  op1[2] = (int)((w[3] << 4) & 0xF0F0F0F0u);
-  op1[3] = (int)(w[3] & 0xF0F0F0F0u);
-}
-
 // LDS slot of 16-byte piece p (0..7) of tile row r (an involution in p).
 // Rows are 128 bytes, so rows 2t and 2t+1 share a 256-byte bank window;
 // xoring with t spreads 16 consecutive rows over all 16 slots of the window.
 __device__ __forceinline__ int swz(int r, int p) { return p ^ ((r >> 1) & 7); }
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // A compile-time range [LO, HI) of DMA wave-instructions.
 template <int LO, int HI>
@@ -84,9 +65,6 @@ struct DmaRange {
   static constexpr int lo = LO, hi = HI;
 };
 using NoDma = DmaRange<0, 0>;
-
-// s_waitcnt lgkmcnt(0), vmcnt and expcnt left alone.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Map the linear block id to a (tile_m, tile_n): consecutive hardware block
 // ids go to different XCDs (round robin over 8), so first regroup them so
@@ -263,9 +241,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   auto widen_into = [&](int rbuf, int obuf) __attribute__((always_inline)) {
     if constexpr (CB == 4) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) widen(rawA[rbuf][i], opA[obuf][i][0], opA[obuf][i][1]);
+      for (int i = 0; i < FM; ++i) widen_hi_nibble(rawA[rbuf][i], opA[obuf][i][0], opA[obuf][i][1]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) widen(rawB[rbuf][j], opB[obuf][j][0], opB[obuf][j][1]);
+      for (int j = 0; j < FN; ++j) widen_hi_nibble(rawB[rbuf][j], opB[obuf][j][0], opB[obuf][j][1]);
     } else {
 #pragma unroll
       for (int i = 0; i < FM; ++i) opA[obuf][i][0] = __builtin_bit_cast(v4i, rawA[rbuf][i]);
@@ -294,7 +272,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
           // DMA instructions spaced evenly over the chunk's MFMAs: after
           // MFMA idx when idx is a multiple of the spacing
           constexpr int NMF = KS * FM * FN, ND = Q_HI - Q_LO;
-          constexpr int SP = ND > 0 ? (NMF / ND > 0 ? NMF / ND : 1) : 1;
+          constexpr int SP = ND > 0 && NMF / (ND > 0 ? ND : 1) > 0 ? NMF / (ND > 0 ? ND : 1) : 1;
           const int idx = (ks * FM + i) * FN + j;
           if (idx % SP == 0 && idx / SP < ND) issue_q(dkt, dstage, Q_LO + idx / SP);
         }
@@ -317,7 +295,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
     if constexpr (DO_WIDEN) widen_into(rbuf, 1 - obuf);
     // order: MFMAs with the DMA instructions spread evenly between them and
     // the widening VALU work shared out
-    constexpr int SP = ND > 0 ? (NMFMA / ND > 0 ? NMFMA / ND : 1) : 1;
+    constexpr int SP = ND > 0 && NMFMA / (ND > 0 ? ND : 1) > 0 ? NMFMA / (ND > 0 ? ND : 1) : 1;
 #pragma unroll
     for (int k = 0; k < NMFMA; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -614,9 +592,7 @@ hipError_t launch_prefill(const uint8_t *a, const float *sa, const uint8_t *w, c
                           hipStream_t stream) {
   if (group != 0)
     return launch_cfg<128, 128, 2, 2, 2, true, CB>(a, sa, w, sw, M, N, K, group, y, ld_y, out_i32, stream);
-  int dev = 0, cus = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = device_cu_count();
   // fraction of the busy slot-rounds doing useful work, times the fraction of
   // the tile area inside the matrix, times a mild preference for bigger tiles
   auto score = [&](int64_t bm, int64_t bn, int64_t per_cu, double size_pref) __attribute__((always_inline)) {

@@ -31,16 +31,6 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-__device__ __forceinline__ void swap16u(unsigned &a, unsigned &b) {
-  auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
-}
-__device__ __forceinline__ void swap32u(unsigned &a, unsigned &b) {
-  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
-}
 // max / min over the four lanes c16 + 16 g (lane bits 4 and 5)
 __device__ __forceinline__ float max_g(float v) {
   auto a = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
@@ -211,10 +201,7 @@ namespace {
 template <bool SIGNS>
 hipError_t launch_kv(const void *kv, int64_t T, int64_t H, int64_t ld_kv, const int8_t *signs, uint8_t *codes,
                      float *scales, uint8_t *zeros, hipStream_t stream) {
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  int cus = 256;
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = device_cu_count();
   // persistent grid: as many blocks as are resident at once, each wave
   // walking its tiles with the next two in flight
   // resident blocks per CU: a constant of the kernel, queried once (a

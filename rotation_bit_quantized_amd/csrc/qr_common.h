@@ -90,6 +90,32 @@ __device__ __forceinline__ void swap32(float &a, float &b) {
   a = u2f(r[0]);
   b = u2f(r[1]);
 }
+__device__ __forceinline__ void swap16u(unsigned &a, unsigned &b) {
+  auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap32u(unsigned &a, unsigned &b) {
+  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// 32 packed 4-bit codes (16 bytes) -> two int8 MFMA operands of 16 values
+// 16 q each, in "high-nibble" form: lo = (w << 4) & 0xF0F0F0F0 and
+// hi = w & 0xF0F0F0F0 (exact for q in [-8, 7], three VALU ops per 8 codes).
+// The k order inside a dword is permuted; widening both GEMM operands the
+// same way makes the permutation cancel, and the sum carries 256 q_a q_w.
+__device__ __forceinline__ void widen_hi_nibble(const v4u &w, v4i &op0, v4i &op1) {
+  op0[0] = (int)((w[0] << 4) & 0xF0F0F0F0u);
+  op0[1] = (int)(w[0] & 0xF0F0F0F0u);
+  op0[2] = (int)((w[1] << 4) & 0xF0F0F0F0u);
+  op0[3] = (int)(w[1] & 0xF0F0F0F0u);
+  op1[0] = (int)((w[2] << 4) & 0xF0F0F0F0u);
+  op1[1] = (int)(w[2] & 0xF0F0F0F0u);
+  op1[2] = (int)((w[3] << 4) & 0xF0F0F0F0u);
+  op1[3] = (int)(w[3] & 0xF0F0F0F0u);
+}
 
 template <int CTRL>
 __device__ __forceinline__ unsigned dpp(unsigned v) {

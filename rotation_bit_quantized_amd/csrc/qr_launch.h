@@ -6,7 +6,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qr {
+
+// Compute units of the current device.  Queried once per device and kept:
+// the launch code sits on the host path of latency-bound calls.
+inline int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 struct RotArgs {
   int n;          // row width

@@ -163,9 +163,22 @@ hipError_t launch_rq_generic_full(const void *x, const void *up, int64_t rows, i
   const bool two_copies = r.dense_m > kInPlaceM;
   const size_t lds = sizeof(float) * ((two_copies ? 2 * (size_t)r.n : (size_t)r.n) + (size_t)(r.n / g));
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void *)rq_generic_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // the kernel's dynamic LDS limit, raised once per device to the largest
+    // size asked for so far (not on every launch)
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> raised[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices || raised[dev].load(std::memory_order_relaxed) < (int)lds) {
+      e = hipFuncSetAttribute((const void *)rq_generic_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      if (dev >= 0 && dev < kMaxDevices) {
+        int cur = raised[dev].load(std::memory_order_relaxed);
+        while (cur < (int)lds && !raised[dev].compare_exchange_weak(cur, (int)lds)) {
+        }
+      }
+    }
   }
   const int64_t grid = rows < 4096 ? rows : 4096;
   const float scale_mul = (float)(1.0 / ((double)qmax * __builtin_sqrt((double)r.had_n)));

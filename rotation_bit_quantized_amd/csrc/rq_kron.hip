@@ -307,9 +307,7 @@ bool rq_kron_supported(const RotArgs &r, int group) {
 hipError_t launch_rq_kron(const void *x, int64_t rows, int64_t ld_x, const RotArgs &r, int group,
                           uint8_t *codes, float *scales, hipStream_t stream) {
   (void)group;
-  int dev = 0, cus = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = device_cu_count();
   const float scale_mul = (float)(1.0 / (7.0 * 8.0));   // 1/(7 sqrt(64))
   const int64_t grid = rows < 2 * cus ? rows : 2 * cus;   // two blocks per CU
   rq_kron_kernel<<<dim3((unsigned)grid), dim3(64 * kWaves), 0, stream>>>(

@@ -301,9 +301,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron4096_kernel(
 template <int M, bool FUSED>
 hipError_t launch_m(const void *x, const void *up, int64_t rows, int64_t ld_x, const float *dense, uint8_t *codes,
                     float *scales, hipStream_t stream) {
-  int dev = 0, cus = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = device_cu_count();
   // resident blocks per CU: a constant of the kernel, queried once (a
   // function-local static is initialised exactly once, thread-safely)
   static const int per_cu = [] {

@@ -39,26 +39,6 @@
 namespace qr {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void swap16(float &a, float &b) {
-  auto r = __builtin_amdgcn_permlane16_swap(f2u(a), f2u(b), false, false);
-  a = u2f(r[0]);
-  b = u2f(r[1]);
-}
-__device__ __forceinline__ void swap32(float &a, float &b) {
-  auto r = __builtin_amdgcn_permlane32_swap(f2u(a), f2u(b), false, false);
-  a = u2f(r[0]);
-  b = u2f(r[1]);
-}
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // n = 4096: four waves per block, each with two row buffers (two of its
 // rows stream in while it works on a third): 64 KB per block, two blocks per
 // CU.  n = 8192: eight waves per block, each with one row buffer refilled as
@@ -416,10 +396,7 @@ __global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
 template <int L, int GROUP, int BITS = 4>
 hipError_t launch_one(const void *x, int64_t rows, int64_t ld_x, const int8_t *signs, uint8_t *codes,
                       float *scales, hipStream_t stream) {
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  int cus = 256;
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = device_cu_count();
   // persistent grid: as many blocks as are resident at once
   // resident blocks per CU: a constant of the kernel, queried once (a
   // function-local static is initialised exactly once, thread-safely)

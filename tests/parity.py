@@ -8,7 +8,9 @@ CPU oracle under the stated tolerances.
   on a rounding boundary to within fp32 error can round differently.)
 * Integer GEMM sums: bit-exact.
 * fp16 outputs: relative Frobenius error <= OUT_REL_FRO against the oracle's
-  fp64 dequantized output from the oracle's codes.
+  fp64 dequantized output from the oracle's codes; where both sides are fed
+  the same codes, every element within epilogue_bound (one fp16 rounding
+  plus the fp32 roundings of the epilogue).
 * Scales: relative error <= SCALE_RTOL (fp32 transform vs fp64).
 * Decode attention outputs (fp16): per (sequence, head) relative Frobenius
   error <= ATTN_REL_FRO and every element within ATTN_ABS_FRAC of that head's
@@ -75,6 +77,31 @@ def check_output(gpu_fp16: np.ndarray, ref: np.ndarray, what: str = "output"):
     e = rel_fro(gpu_fp16.astype(np.float64), ref)
     assert e <= OUT_REL_FRO, f"{what}: relative Frobenius error {e:.3e}"
     return e
+
+
+def epilogue_bound(acc, sx, sw, group: int = 0) -> np.ndarray:
+    """Largest |y_gpu - y_oracle| per element of a GEMM output computed from
+    the same integer sums.  The epilogue forms each term acc_j * s_x * s_w in
+    fp32 (the integer converted to fp32, the scale product and the term: at
+    most three roundings of 2^-24), adds the G terms of a grouped output in
+    fp32 (G - 1 more), and rounds the result to fp16 (half an ulp: 2^-11
+    relative, or 2^-25 absolute below the normal range).  With T the sum of
+    the terms' magnitudes, the fp32 value v is within e32 = (G + 3) 2^-24 T of
+    the exact y, and |fp16(v) - y| <= 2^-11 (|y| + e32) + e32 + 2^-25."""
+    acc = np.asarray(acc, np.float64)
+    sx = np.asarray(sx, np.float64)
+    sw = np.asarray(sw, np.float64)
+    if group == 0:
+        exact = acc * sx[:, None] * sw[None, :]
+        terms = np.abs(exact)
+        g = 1
+    else:
+        parts = acc * np.transpose(sx)[:, :, None] * np.transpose(sw)[:, None, :]   # [G, M, N]
+        exact = parts.sum(axis=0)
+        terms = np.abs(parts).sum(axis=0)
+        g = acc.shape[0]
+    e32 = (g + 3) * 2.0 ** -24 * terms
+    return 2.0 ** -11 * (np.abs(exact) + e32) + e32 + 2.0 ** -25
 
 
 def check_kv(gpu_codes, gpu_step, gpu_zero, kv, signs=None):

@@ -140,8 +140,8 @@ def test_kv_empty_is_noop():
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(4, 4096, dtype=torch.float16)
-    with pytest.raises(ValueError):
-        qr.rotate_quant(x, object())
+    with pytest.raises(ValueError, match="live on the GPU"):
+        qr.rotate_quant(x, qr.Rotation.hadamard(4096, device="cpu"))
 
 
 def _attn(lib, **a):
@@ -235,3 +235,121 @@ def test_swiglu_rejects():
     assert call(ld=28000) == qr.QR_ESHAPE
     assert call(rows=-1) == qr.QR_EINVAL
     assert call(rows=0, g=None, u=None) == qr.QR_OK
+
+
+def test_gemm_k_bound_is_exclusive():
+    """Products of widened codes reach 2^14 (q = -8 on both sides, or int8
+    codes of -128): K = 2^17 would sum to exactly 2^31 and wrap, so the
+    largest K accepted is 2^17 - 128 (validated on the host; the accepted
+    sizes are not launched here)."""
+    lib = qr.library()
+    K = 1 << 17
+    assert lib.qr_int4_gemm(A16, A16, A16, A16, 128, 128, K, 0, A16, 128, None) == qr.QR_ESHAPE
+    assert lib.qr_int4_gemm_i32(A16, A16, 128, 128, K, 0, A16, None) == qr.QR_ESHAPE
+    assert lib.qr_int8_gemm(A16, A16, A16, A16, 128, 128, K, 0, A16, 128, None) == qr.QR_ESHAPE
+    assert lib.qr_int8_gemm_i32(A16, A16, 128, 128, K, 0, A16, None) == qr.QR_ESHAPE
+    assert lib.qr_int4_gemm(A16, A16, A16, A16, 16, 128, K, 0, A16, 128, None) == qr.QR_ESHAPE   # decode size
+
+
+# ---- the Python binding validates shapes and layouts before any launch.
+# These run on CPU tensors: every shape check comes before the check that the
+# tensors live on the GPU, so a wrong shape is reported as such.
+
+def _cpu(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_rotation_checks():
+    import torch
+    with pytest.raises(ValueError, match="signs must hold"):
+        qr.Rotation(4096, 4096, signs=torch.ones(4095, dtype=torch.int8), device="cpu")
+    with pytest.raises(ValueError, match="square"):
+        qr.Rotation(64 * 6, 64, dense=torch.zeros(6, 5), device="cpu")
+    with pytest.raises(ValueError, match="had_n"):
+        qr.Rotation(4096, 2048, device="cpu")
+
+
+def test_binding_rotate_quant_checks():
+    import torch
+    rot = qr.Rotation(512, 512, device="cpu")
+    x = _cpu((4, 512), torch.float16)
+    with pytest.raises(ValueError, match="columns"):
+        qr.rotate_quant(_cpu((4, 520), torch.float16), rot)
+    with pytest.raises(ValueError, match="unit column stride"):
+        qr.rotate_quant(_cpu((512, 4), torch.float16).t(), rot)
+    with pytest.raises(ValueError, match="codes must have shape"):
+        qr.rotate_quant(x, rot, codes=_cpu((4, 255), torch.uint8))
+    with pytest.raises(ValueError, match="codes must be contiguous"):
+        qr.rotate_quant(x, rot, codes=_cpu((4, 512), torch.uint8)[:, ::2])
+    with pytest.raises(ValueError, match="scales must have shape"):
+        qr.rotate_quant(x, rot, group=128, scales=_cpu((4,), torch.float32))
+    with pytest.raises(ValueError, match="group"):
+        qr.rotate_quant(x, rot, group=100)
+    with pytest.raises(TypeError, match="Rotation"):
+        qr.rotate_quant(x, object())
+    with pytest.raises(ValueError, match="live on the GPU"):
+        qr.rotate_quant(x, rot)
+    with pytest.raises(ValueError, match="codes must have shape"):
+        qr.rotate_quant_i8(x, rot, 8, codes=_cpu((4, 256), torch.int8))
+
+
+def test_binding_gemm_checks():
+    import torch
+    a, w = _cpu((130, 256), torch.uint8), _cpu((70, 256), torch.uint8)
+    sa, sw = _cpu((130,), torch.float32), _cpu((70,), torch.float32)
+    with pytest.raises(ValueError, match="K mismatch"):
+        qr.int4_gemm(a, sa, _cpu((70, 128), torch.uint8), sw)
+    with pytest.raises(ValueError, match="contiguous"):
+        qr.int4_gemm(_cpu((130, 512), torch.uint8)[:, :256], sa, w, sw)
+    with pytest.raises(ValueError, match="scales must hold"):
+        qr.int4_gemm(a, _cpu((129,), torch.float32), w, sw)
+    with pytest.raises(ValueError, match="scales must hold"):
+        qr.int4_gemm(a, sa, w, sw, group=128)                 # group scales are [M][K/128]
+    with pytest.raises(ValueError, match="group"):
+        qr.int4_gemm(a, sa, w, sw, group=384)
+    with pytest.raises(ValueError, match="y must have shape"):
+        qr.int4_gemm(a, sa, w, sw, y=_cpu((130, 69), torch.float16))
+    with pytest.raises(ValueError, match="acc must have shape"):
+        qr.int4_gemm_i32(a, w, group=128, acc=_cpu((130, 70), torch.int32))
+    with pytest.raises(ValueError, match="live on the GPU"):
+        qr.int4_gemm(a, sa, w, sw)
+    with pytest.raises(TypeError, match="int8"):
+        qr.int8_gemm(a, sa, w, sw)
+
+
+def test_binding_kv_and_attention_checks():
+    import torch
+    kv = _cpu((4, 2, 128), torch.float16)
+    with pytest.raises(ValueError, match="hold"):
+        qr.kv_quant(kv, codes=_cpu((4, 2, 63), torch.uint8))
+    with pytest.raises(ValueError, match="signs must hold"):
+        qr.kv_quant(kv, signs=torch.ones(64, dtype=torch.int8))
+    with pytest.raises(ValueError, match="contiguous heads"):
+        qr.kv_quant(_cpu((4, 128, 2), torch.float16).transpose(1, 2))
+    B, T, Hq, Hkv = 2, 8, 4, 2
+    q = _cpu((B, Hq, 128), torch.float16)
+    kc, vc = _cpu((B, T, Hkv, 64), torch.uint8), _cpu((B, T, Hkv, 64), torch.uint8)
+    ks, vs = _cpu((B, T, Hkv), torch.float32), _cpu((B, T, Hkv), torch.float32)
+    kz, vz = _cpu((B, T, Hkv), torch.uint8), _cpu((B, T, Hkv), torch.uint8)
+    with pytest.raises(ValueError, match="v_scales must hold"):
+        qr.kv_attn_decode(q, kc, ks, kz, vc, _cpu((B, T - 1, Hkv), torch.float32), vz, workspace=False)
+    with pytest.raises(ValueError, match="lens must hold"):
+        qr.kv_attn_decode(q, kc, ks, kz, vc, vs, vz, lens=[1, 2, 3], workspace=False)
+    with pytest.raises(ValueError, match="out must have shape"):
+        qr.kv_attn_decode(q, kc, ks, kz, vc, vs, vz, out=_cpu((B, Hq, 64), torch.float16), workspace=False)
+    with pytest.raises(ValueError, match="batch"):
+        qr.kv_attn_decode(_cpu((3, Hq, 128), torch.float16), kc, ks, kz, vc, vs, vz, workspace=False)
+    with pytest.raises(ValueError, match="live on the GPU"):
+        qr.kv_attn_decode(q, kc, ks, kz, vc, vs, vz, workspace=False)
+
+
+def test_binding_swiglu_checks():
+    import torch
+    rot = qr.Rotation(512, 512, device="cpu")
+    g = _cpu((4, 512), torch.float16)
+    with pytest.raises(ValueError, match="up must have shape"):
+        qr.swiglu_rotate_quant(g, _cpu((3, 512), torch.float16), rot)
+    both = _cpu((4, 1536), torch.float16)
+    with pytest.raises(ValueError, match="one row stride"):
+        qr.swiglu_rotate_quant(both[:, :512], _cpu((4, 512), torch.float16), rot)

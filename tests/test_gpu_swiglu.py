@@ -10,14 +10,16 @@ lies within 2^-20 of an fp16 rounding midpoint both neighbours are valid.
 y is linear in x, so a different choice at such elements k moves output j by
 at most B_j = sum_k ulp_k |R[k, j]|: a code may then differ where the
 pre-rounding value y_j / s lies within B_j / s of a .5 boundary (besides the
-usual window), and the scale max|y| / 7 by at most max_j B_j / 7."""
+usual window), and the scale max|y| / 7 by at most max_j B_j / 7.  Mismatches
+that this does not explain (inside the usual window only) are capped at the
+usual fraction of the elements."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import workloads as W
-from tests.parity import SCALE_RTOL, check_symmetric_codes, near_half
+from tests.parity import MAX_MISMATCH_FRAC, SCALE_RTOL, check_symmetric_codes, near_half
 
 pytestmark = pytest.mark.gpu
 
@@ -70,8 +72,14 @@ def run_and_check(qr, gate, up, n, had_n, dense=None, signs=None, group=0):
     gq = O.unpack_int4(host(codes))
     mism = gq != q
     frac = np.abs(np.abs(t - np.floor(t)) - 0.5)
-    unexplained = mism & ~near_half(t) & ~(frac <= shift)
+    explained_by_x = frac <= shift
+    unexplained = mism & ~near_half(t) & ~explained_by_x
     assert not unexplained.any(), f"{int(unexplained.sum())} code mismatches beyond the boundary and rounding bounds"
+    # the rotated-value roundings: boundary mismatches that the fp16 choice
+    # of x does not explain are capped as for every other code
+    boundary_only = mism & ~explained_by_x
+    assert boundary_only.sum() <= MAX_MISMATCH_FRAC * mism.size, \
+        f"{int(boundary_only.sum())} boundary mismatches of {mism.size}"
     assert np.all(np.abs(gq.astype(np.int64) - q) <= 1)
     gs = host(scales).astype(np.float64).reshape(np.asarray(s).shape)
     sref = np.asarray(s, np.float64)
