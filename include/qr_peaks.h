@@ -1,0 +1,46 @@
+/*
+ * qr_peaks.h - measurement probes of libqr: what this GPU attains for a
+ * streaming copy and for back-to-back dense MFMAs.  The benchmark puts every
+ * hot-path kernel against these measured ceilings beside the datasheet peaks
+ * (HBM 8 TB/s, int8 MFMA 5.0 POP/s, fp16 MFMA 2.5 PFLOP/s).  They compute
+ * nothing of the method.  Pointers are device pointers; calls are
+ * asynchronous on `stream` and validate their arguments on the host first.
+ */
+#ifndef QR_PEAKS_H
+#define QR_PEAKS_H
+
+#include <stdint.h>
+
+#include "qr.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Copy `bytes` (a multiple of 16) from src to dst, both 16-byte aligned and
+ * not overlapping: 16-byte nontemporal loads and stores, four loads in
+ * flight per lane, persistent grid.  HBM traffic = 2 * bytes.
+ */
+qr_status qr_peak_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
+/*
+ * Number of waves qr_peak_mfma launches on the current device (8 per CU);
+ * `out` must hold 64 int32 per wave.
+ */
+int64_t qr_peak_mfma_waves(void);
+
+/*
+ * Every wave issues `iters` (1 .. 2^24) rounds of four independent MFMAs with
+ * no memory traffic: kind 0 = v_mfma_i32_32x32x32_i8 (65536 int8 ops each),
+ * kind 1 = v_mfma_f32_16x16x32_f16 (16384 fp16 flops each).  Work per call =
+ * waves * iters * 4 * (ops per MFMA).  `out` receives one checksum per lane
+ * (so the loop cannot be removed), int32 [waves * 64], 4-byte aligned.
+ */
+qr_status qr_peak_mfma(int64_t kind, int64_t iters, int32_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QR_PEAKS_H */

@@ -23,6 +23,7 @@ __all__ = [
     "QRError", "LibraryNotBuilt", "Rotation", "library", "library_path", "rotate_quant", "int4_gemm",
     "int4_gemm_i32", "kv_quant", "kv_attn_decode", "kv_attn_decode_workspace", "rotate_quant_i8",
     "int8_gemm", "int8_gemm_i32", "swiglu_rotate_quant", "status_str", "version", "EXPORTS",
+    "peak_copy", "peak_mfma",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,8 +32,10 @@ _lib = None
 
 QR_OK, QR_EINVAL, QR_ESHAPE, QR_EALIGN, QR_EDEVICE = 0, 1, 2, 3, 4
 EXPORTS = ("qr_rotate_quant", "qr_int4_gemm", "qr_kv_quant", "qr_int4_gemm_i32", "qr_kv_attn_decode",
-           "qr_kv_attn_decode_workspace", "qr_rotate_quant_i8", "qr_int8_gemm", "qr_int8_gemm_i32",
-           "qr_swiglu_rotate_quant", "qr_status_str", "qr_version")
+           "qr_kv_attn_decode_workspace", "qr_rotate_quant_i8", "qr_int8_gemm",
+           "qr_int8_gemm_i32", "qr_swiglu_rotate_quant", "qr_status_str", "qr_version",
+           # measurement probes (include/qr_peaks.h)
+           "qr_peak_copy", "qr_peak_mfma", "qr_peak_mfma_waves")
 
 
 class QRError(RuntimeError):
@@ -84,6 +87,12 @@ def library():
     lib.qr_int8_gemm_i32.restype = st
     lib.qr_swiglu_rotate_quant.argtypes = [vp, vp, i64, i64, ctypes.POINTER(_Rot), i64, vp, vp, vp]
     lib.qr_swiglu_rotate_quant.restype = st
+    lib.qr_peak_copy.argtypes = [vp, vp, i64, vp]
+    lib.qr_peak_copy.restype = st
+    lib.qr_peak_mfma.argtypes = [i64, i64, vp, vp]
+    lib.qr_peak_mfma.restype = st
+    lib.qr_peak_mfma_waves.argtypes = []
+    lib.qr_peak_mfma_waves.restype = i64
     lib.qr_status_str.argtypes = [st]
     lib.qr_status_str.restype = ctypes.c_char_p
     lib.qr_version.argtypes = []
@@ -468,3 +477,27 @@ def swiglu_rotate_quant(gate: torch.Tensor, up: torch.Tensor, rot: Rotation, gro
                                           _ptr(codes), _ptr(scales), _stream(stream))
     _check("qr_swiglu_rotate_quant", st)
     return codes, scales
+
+
+# ---- measurement probes (include/qr_peaks.h): attainable copy and MFMA rates
+
+def peak_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """qr_peak_copy: stream src into dst (equal byte sizes, contiguous, GPU)."""
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_contiguous() and dst.is_contiguous()) or dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must be contiguous and of equal byte size")
+    _on_gpu(src=src, dst=dst)
+    _check("qr_peak_copy", library().qr_peak_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def peak_mfma(kind: int, iters: int, out=None, stream=None):
+    """qr_peak_mfma: kind 0 = int8 32x32x32, 1 = fp16 16x16x32.  Returns
+    (out, ops per call)."""
+    waves = int(library().qr_peak_mfma_waves())
+    if out is None:
+        out = torch.empty((waves * 64,), dtype=torch.int32, device="cuda")
+    _need(out, torch.int32, "out", (waves * 64,), True)
+    _on_gpu(out=out)
+    _check("qr_peak_mfma", library().qr_peak_mfma(int(kind), int(iters), _ptr(out), _stream(stream)))
+    per = 65536 if kind == 0 else 16384
+    return out, waves * int(iters) * 4 * per

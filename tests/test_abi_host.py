@@ -13,19 +13,31 @@ import pytest
 import rotation_bit_quantized_amd as qr
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "qr.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("qr.h", "qr_peaks.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(qr.library_path()), reason="libqr.so not built")
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = "".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(qr_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(qr.EXPORTS)
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(os.path.basename(h) for h in HEADERS)
+
+
+def test_peak_probes_reject_bad_arguments():
+    lib = qr.library()
+    assert lib.qr_peak_copy(A16, A16, 100, None) == qr.QR_ESHAPE
+    assert lib.qr_peak_copy(MIS, A16, 1024, None) == qr.QR_EALIGN
+    assert lib.qr_peak_copy(None, A16, 1024, None) == qr.QR_EINVAL
+    assert lib.qr_peak_copy(None, None, 0, None) == qr.QR_OK
+    assert lib.qr_peak_mfma(2, 10, A16, None) == qr.QR_EINVAL
+    assert lib.qr_peak_mfma(0, 0, A16, None) == qr.QR_ESHAPE
+    assert lib.qr_peak_mfma(0, 10, None, None) == qr.QR_EINVAL
 
 
 def test_library_exports_every_declared_symbol():
@@ -353,3 +365,4 @@ def test_binding_swiglu_checks():
     both = _cpu((4, 1536), torch.float16)
     with pytest.raises(ValueError, match="one row stride"):
         qr.swiglu_rotate_quant(both[:, :512], _cpu((4, 512), torch.float16), rot)
+

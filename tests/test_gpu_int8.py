@@ -41,6 +41,8 @@ def host(t):
     (192, 256, 1024, 128),    # group-wise: a group is one K-tile
     (150, 160, 1152, 384),    # groups of three K-tiles
     (300, 200, 640, 0),       # K an odd multiple of 128
+    (33, 4100, 11008, 0),     # decode: three token tiles, eleven K chunks (the last a partial one)
+    (16, 48, 130944, 0),      # decode at the largest K: the -128 rows reach 2^31 - 2^21
 ])
 def test_int8_gemm_i32_exact(qr, M, N, K, group):
     qa = W.make_random_codes(M, K, seed=7 * M + K, lo=-128, hi=127)

@@ -253,6 +253,9 @@ def test_weight_prep_on_gpu_matches_oracle(qr, cfg, ncols):
     (192, 256, 640, 128),     # group-wise with the half tile
     (150, 160, 1152, 384),    # groups that straddle K-tiles, half tile at the end
     (100, 96, 1536, 768),     # groups of three K-tiles
+    (33, 4100, 11008, 0),     # decode: three token tiles, six K chunks (the last a partial one), ragged N
+    (16, 48, 130944, 0),      # decode: the largest K; the -8 rows reach 2^31 - 2^21 in the widened int32 sums
+    (130, 70, 130944, 0),     # prefill at the largest K (a half K-tile at the end)
 ])
 def test_gemm_i32_exact(qr, M, N, K, group):
     qa = W.make_random_codes(M, K, seed=M + K)
