@@ -42,7 +42,8 @@ typedef enum {
   QR_EINVAL = 1,   /* null pointer, bad enum value, negative size        */
   QR_ESHAPE = 2,   /* sizes the operation does not support               */
   QR_EALIGN = 3,   /* pointer or leading dimension not aligned as needed */
-  QR_EDEVICE = 4   /* the HIP runtime reported an error at launch        */
+  QR_EDEVICE = 4,  /* the HIP runtime reported an error at launch        */
+  QR_ESCRATCH = 5  /* more scratch than qr_kv_attn_decode_noalloc holds  */
 } qr_status;
 
 /*
@@ -244,6 +245,28 @@ qr_status qr_kv_attn_decode(const void *q_f16, int64_t B, int64_t Hq, int64_t Hk
                             const uint8_t *v_zeros, const int32_t *lens, const int8_t *signs,
                             float sm_scale, void *workspace, int64_t workspace_bytes, void *out_f16,
                             void *stream);
+
+/*
+ * qr_kv_attn_decode for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * plan, kernels and results as qr_kv_attn_decode with a workspace of
+ * qr_kv_attn_decode_workspace(...) bytes, with the split partials kept in a
+ * static device array of the library instead (16 MiB per GPU, part of the
+ * library's code object, held until the process ends).  Nothing is
+ * allocated and no library routine that allocates is called.
+ * Arguments as for qr_kv_attn_decode without the workspace.  A shape whose
+ * workspace would exceed 16 MiB (16777216 bytes) returns QR_ESCRATCH and
+ * launches nothing.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams, other host threads) race and give
+ * undefined results; calls ordered on one stream are safe.  The first call on
+ * a device looks up the array's device address (hipGetSymbolAddress) with
+ * that device current.
+ */
+qr_status qr_kv_attn_decode_noalloc(const void *q_f16, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                                    int64_t head_dim, const uint8_t *k_codes, const float *k_scales,
+                                    const uint8_t *k_zeros, const uint8_t *v_codes, const float *v_scales,
+                                    const uint8_t *v_zeros, const int32_t *lens, const int8_t *signs,
+                                    float sm_scale, void *out_f16, void *stream);
 
 /*
  * Workspace bytes qr_kv_attn_decode needs for this shape (0: none).  Depends

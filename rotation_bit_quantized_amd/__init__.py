@@ -30,9 +30,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqr.so")
 _lib = None
 
-QR_OK, QR_EINVAL, QR_ESHAPE, QR_EALIGN, QR_EDEVICE = 0, 1, 2, 3, 4
+QR_OK, QR_EINVAL, QR_ESHAPE, QR_EALIGN, QR_EDEVICE, QR_ESCRATCH = 0, 1, 2, 3, 4, 5
 EXPORTS = ("qr_rotate_quant", "qr_int4_gemm", "qr_kv_quant", "qr_int4_gemm_i32", "qr_kv_attn_decode",
-           "qr_kv_attn_decode_workspace", "qr_rotate_quant_i8", "qr_int8_gemm",
+           "qr_kv_attn_decode_workspace", "qr_kv_attn_decode_noalloc", "qr_rotate_quant_i8", "qr_int8_gemm",
            "qr_int8_gemm_i32", "qr_swiglu_rotate_quant", "qr_status_str", "qr_version",
            # measurement probes (include/qr_peaks.h)
            "qr_peak_copy", "qr_peak_mfma", "qr_peak_mfma_waves")
@@ -77,6 +77,9 @@ def library():
     lib.qr_kv_attn_decode.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_float, vp, i64, vp, vp]
     lib.qr_kv_attn_decode.restype = st
+    lib.qr_kv_attn_decode_noalloc.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              ctypes.c_float, vp, vp]
+    lib.qr_kv_attn_decode_noalloc.restype = st
     lib.qr_kv_attn_decode_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.qr_kv_attn_decode_workspace.restype = st
     lib.qr_rotate_quant_i8.argtypes = [vp, i64, i64, ctypes.POINTER(_Rot), i64, i64, vp, vp, vp]

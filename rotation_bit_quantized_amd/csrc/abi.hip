@@ -4,7 +4,41 @@
 #include "../../include/qr.h"
 #include "qr_launch.h"
 
+#include <atomic>
+#include <mutex>
+
+// Scratch memory of qr_kv_attn_decode_noalloc (the split partials of decode
+// attention): one copy per GPU, part of the library's code object, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: the device address is taken with hipGetSymbolAddress, once
+// per device, and only that pointer is ever handed to a kernel.
+constexpr int64_t kScratchBytes = (int64_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];            // written once per device under g_scratch_mu
+std::atomic<bool> g_scratch_ready[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on the
+// first call on that device, with that device current).
+qr_status scratch_on_current_device(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QR_EDEVICE;
+  if (!g_scratch_ready[dev].load(std::memory_order_acquire)) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ready[dev].load(std::memory_order_relaxed)) {
+      void *p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return QR_EDEVICE;
+      g_scratch_ptr[dev] = p;
+      g_scratch_ready[dev].store(true, std::memory_order_release);
+    }
+  }
+  *ptr = g_scratch_ptr[dev];
+  return QR_OK;
+}
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 inline bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -72,6 +106,7 @@ const char *qr_status_str(qr_status s) {
     case QR_ESHAPE: return "unsupported shape";
     case QR_EALIGN: return "misaligned pointer or leading dimension";
     case QR_EDEVICE: return "HIP runtime error at launch";
+    case QR_ESCRATCH: return "the call needs more scratch memory than the library's static buffer holds";
   }
   return "unknown status";
 }
@@ -260,6 +295,31 @@ qr_status qr_kv_attn_decode(const void *q_f16, int64_t B, int64_t Hq, int64_t Hk
   }
   return from_hip(qr::launch_attn_decode(q_f16, B, Hq, Hkv, T, k_codes, k_scales, k_zeros, v_codes, v_scales,
                                          v_zeros, lens, signs, sm_scale, plan, (float *)workspace, out_f16,
+                                         (hipStream_t)stream));
+}
+
+qr_status qr_kv_attn_decode_noalloc(const void *q_f16, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                                    int64_t head_dim, const uint8_t *k_codes, const float *k_scales,
+                                    const uint8_t *k_zeros, const uint8_t *v_codes, const float *v_scales,
+                                    const uint8_t *v_zeros, const int32_t *lens, const int8_t *signs,
+                                    float sm_scale, void *out_f16, void *stream) {
+  qr_status st = check_attn(q_f16, B, Hq, Hkv, T, head_dim, k_codes, k_scales, k_zeros, v_codes, v_scales,
+                            v_zeros, lens, signs, sm_scale, out_f16);
+  if (st != QR_OK) return st;
+  if (B == 0 || Hq == 0) return QR_OK;
+  // the same plan (and so the same kernels and results) as qr_kv_attn_decode
+  // with a workspace; the split partials go to the static scratch array
+  const qr::AttnPlan plan = qr::attn_decode_plan(B, Hq, Hkv, T);
+  if (plan.workspace_bytes > kScratchBytes) return QR_ESCRATCH;
+  void *ws = nullptr;
+  if (plan.splits > 1) {
+    st = scratch_on_current_device(&ws);
+    if (st != QR_OK) return st;
+  }
+  // every partial a launch merges is written by the same launch first: the
+  // scratch needs no clearing between calls
+  return from_hip(qr::launch_attn_decode(q_f16, B, Hq, Hkv, T, k_codes, k_scales, k_zeros, v_codes, v_scales,
+                                         v_zeros, lens, signs, sm_scale, plan, (float *)ws, out_f16,
                                          (hipStream_t)stream));
 }
 

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for s in range(5):
+    for s in range(6):
         assert qr.status_str(s)
     assert qr.status_str(99) == "unknown status"
     assert qr.version() >= 100
@@ -366,3 +366,23 @@ def test_binding_swiglu_checks():
     with pytest.raises(ValueError, match="one row stride"):
         qr.swiglu_rotate_quant(both[:, :512], _cpu((4, 512), torch.float16), rot)
 
+
+def test_attn_noalloc_host_checks():
+    """The allocation-free decode attention validates like qr_kv_attn_decode
+    and rejects, before any launch, a shape whose split partials would not
+    fit its 16 MiB static scratch array."""
+    lib = qr.library()
+    f32 = ctypes.c_float
+
+    def call(B=1, Hq=32, Hkv=32, T=4096, D=128, q=A16, out=A16, kc=A16):
+        return lib.qr_kv_attn_decode_noalloc(q, B, Hq, Hkv, T, D, kc, A16, A16, A16, A16, A16, None, None,
+                                             f32(0.088), out, None)
+
+    assert qr.kv_attn_decode_workspace(512, 64, 64, 4096) > 16 << 20
+    assert call(B=512, Hq=64, Hkv=64) == qr.QR_ESCRATCH
+    assert call(D=64) == qr.QR_ESHAPE
+    assert call(Hkv=3) == qr.QR_ESHAPE
+    assert call(q=None) == qr.QR_EINVAL
+    assert call(kc=MIS) == qr.QR_EALIGN
+    assert call(B=0, q=None, out=None) == qr.QR_OK
+    assert "scratch" in qr.status_str(qr.QR_ESCRATCH)
