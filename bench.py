@@ -84,6 +84,10 @@ def parse():
                     help="read rocprofv3 FETCH_SIZE / WRITE_SIZE runs of `bench.py --config C --copy-calib MIB` "
                          "and add the dominant kernel's HBM bytes per launch to profiles/traffic.json")
     ap.add_argument("--calib-mib", type=int, default=1024, help="size of the copy used with --ingest-pmc")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="digest a rocprofv3 kernel trace of this script (per kernel, all dispatches and the "
+                         "last --trace-last ones) and exit")
+    ap.add_argument("--trace-last", type=int, default=20, help="dispatches of the per-launch timing phase")
     return ap.parse_args()
 
 
@@ -149,12 +153,13 @@ def measure_peaks(dev):
     copy_ms, _ = time_each(lambda i: qr.peak_copy(src, dst), 5, st, warm=1)
     del src, dst
     out = {"hbm_copy_GBs": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1)}
-    for kind, key in ((0, "mfma_int8_TOPS"), (1, "mfma_fp16_TFLOPS")):
+    for kind, key in ((0, "mfma_int8_TOPS"), (1, "mfma_fp16_16x16_TFLOPS"), (2, "mfma_fp16_32x32_TFLOPS")):
         buf, ops = qr.peak_mfma(kind, 20000)
         ms, _ = time_each(lambda i: qr.peak_mfma(kind, 20000, buf), 5, st, warm=1)
         out[key] = round(ops / (ms * 1e-3) / 1e12, 1)
     out["how"] = ("qr_peak_copy of 1 GiB (2 GiB moved); qr_peak_mfma: 8 waves per CU, four independent "
-                  "v_mfma_i32_32x32x32_i8 / v_mfma_f32_16x16x32_f16 chains, 20000 rounds; medians of 5")
+                  "v_mfma_i32_32x32x32_i8 / v_mfma_f32_16x16x32_f16 / v_mfma_f32_32x32x16_f16 chains, "
+                  "20000 rounds; medians of 5")
     return out
 
 
@@ -209,13 +214,22 @@ def cpu_baseline(cfg, rows, kv_rows):
 # ---------------------------------------------------------------- counters
 
 def ingest_pmc(cfg_name, fetch_dir, write_dir, calib_mib):
-    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the step's
-    dominant kernel and of the calibration copy; scale the kernel's by
-    known/measured of the copy (a copy of B bytes reads B and writes B)."""
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the step's GEMM and of its
+    rotate-quant kernel, and of the calibration copy; scale each kernel's by
+    known/measured of the copy (a copy of B bytes reads B and writes B).  The
+    median over a kernel's dispatches is taken, so the one weight-preparation
+    launch of the rotate-quant kernel (another row count) does not count."""
     import csv
     import glob
     import re
-    kernel = "gemm_decode_kernel" if cfg_name == "c5" else "gemm_prefill_kernel"
+    gemm = "gemm_decode_kernel" if cfg_name == "c5" else "gemm_prefill_kernel"
+    cfg = None
+    try:
+        import workloads as W
+        cfg = W.CONFIGS[cfg_name]
+    except Exception:
+        pass
+    rq = "rq_kron_kernel" if cfg is not None and cfg.dense_m > 1 else "rq_pow2_kernel"
 
     def per_dispatch(d, counter):
         vals = {}
@@ -226,11 +240,11 @@ def ingest_pmc(cfg_name, fetch_dir, write_dir, calib_mib):
                     vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
         return vals
 
-    def kernel_avg(vals):
+    def kernel_median(vals, kernel):
         v = [x for (d, k), x in vals.items() if kernel in k]
         if not v:
             raise SystemExit(f"no {kernel} dispatches in the counter data")
-        return sum(v) / len(v), [k for (d, k) in vals if kernel in k][0]
+        return statistics.median(v), len(v), [k for (d, k) in vals if kernel in k][0]
 
     def copy_max(vals):
         v = [x for (d, k), x in vals.items() if "peak_copy" in k]
@@ -239,27 +253,57 @@ def ingest_pmc(cfg_name, fetch_dir, write_dir, calib_mib):
         return max(v)
 
     fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
-    k_fetch, kname = kernel_avg(fetch)
-    k_write, _ = kernel_avg(write)
     known_kib = calib_mib * 1024.0
     f_scale = known_kib / copy_max(fetch)
     w_scale = known_kib / copy_max(write)
-    m = re.search(kernel + r"<[^>]*>", kname)
     try:
         recs = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         recs = {}
-    recs[f"int4_gemm_{cfg_name}"] = {
-        "kernel": m.group(0) if m else kname[:80], "source_hash": source_hash(KERNEL_SOURCES[kernel]),
-        "fetch_bytes": round(k_fetch * 1024 * f_scale), "write_bytes": round(k_write * 1024 * w_scale),
-        "calibration": {"copy": f"qr_peak_copy of {calib_mib} MiB (largest copy dispatch)",
-                        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-                        "raw_fetch_kib": round(k_fetch, 1), "raw_write_kib": round(k_write, 1)},
-        "command": f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 bench.py "
-                   f"--config {cfg_name} --steps 3 --warmup 1 --no-cpu --no-peaks --copy-calib {calib_mib}"}
+    for key, kernel in ((f"int4_gemm_{cfg_name}", gemm), (f"rotate_quant_{cfg_name}", rq)):
+        k_fetch, n, kname = kernel_median(fetch, kernel)
+        k_write, _, _ = kernel_median(write, kernel)
+        m = re.search(kernel + r"<[^>]*>", kname)
+        recs[key] = {
+            "kernel": m.group(0) if m else kernel, "source_hash": source_hash(KERNEL_SOURCES[kernel]),
+            "fetch_bytes": round(k_fetch * 1024 * f_scale), "write_bytes": round(k_write * 1024 * w_scale),
+            "dispatches": n,
+            "calibration": {"copy": f"qr_peak_copy of {calib_mib} MiB (largest copy dispatch)",
+                            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                            "raw_fetch_kib": round(k_fetch, 1), "raw_write_kib": round(k_write, 1)},
+            "command": f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 bench.py "
+                       f"--config {cfg_name} --steps 3 --warmup 1 --no-cpu --no-peaks --copy-calib {calib_mib}"}
+        print(json.dumps({key: recs[key]}))
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     json.dump(recs, open(TRAFFIC_FILE, "w"), indent=1)
-    print(json.dumps(recs[f"int4_gemm_{cfg_name}"]))
+
+
+def trace_summary(path, last):
+    """Digest of a rocprofv3 kernel trace (``*_kernel_trace.csv``): per kernel,
+    the calls, mean / min / max duration over all dispatches, and mean and
+    median over its last `last` dispatches (the per-launch timing phase that
+    follows the timed steps)."""
+    import csv
+    import re
+    per = {}
+    for row in csv.DictReader(open(path)):
+        name = row["Kernel_Name"]
+        name = re.sub(r"^void ", "", name)
+        name = re.sub(r"\(anonymous namespace\)::", "", name)
+        name = re.sub(r"\((?!anonymous).*$", "", name)
+        per.setdefault(name, []).append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
+    lines = [f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'lastN':>6} {'lastN_avg':>10} "
+             f"{'lastN_med':>10}  kernel"]
+    order = sorted(per.items(), key=lambda kv: -sum(e - s for s, e in kv[1]))
+    for name, spans in order:
+        spans.sort()
+        d = [(e - s) / 1e3 for s, e in spans]
+        tail = d[-last:] if len(d) >= last else []
+        lines.append(f"{len(d):>6} {sum(d) / len(d):>10.1f} {min(d):>10.1f} {max(d):>10.1f} "
+                     f"{len(tail) or '-':>6} "
+                     + (f"{sum(tail) / len(tail):>10.1f} {statistics.median(tail):>10.1f}" if tail
+                        else f"{'-':>10} {'-':>10}") + f"  {name[:100]}")
+    print("\n".join(lines))
 
 
 # ---------------------------------------------------------------- the step
@@ -659,6 +703,9 @@ def suite(args):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.trace_last)
+        return
     if args.ingest_pmc:
         ingest_pmc(args.config, args.ingest_pmc[0], args.ingest_pmc[1], args.calib_mib)
         return

@@ -19,8 +19,8 @@ extern "C" {
 
 /*
  * Copy `bytes` (a multiple of 16) from src to dst, both 16-byte aligned and
- * not overlapping: 16-byte nontemporal loads and stores, four loads in
- * flight per lane, persistent grid.  HBM traffic = 2 * bytes.
+ * not overlapping: 16-byte nontemporal loads and stores, eight loads in
+ * flight per lane, one 1024-thread block per CU.  HBM traffic = 2 * bytes.
  */
 qr_status qr_peak_copy(const void *src, void *dst, int64_t bytes, void *stream);
 
@@ -33,7 +33,9 @@ int64_t qr_peak_mfma_waves(void);
 /*
  * Every wave issues `iters` (1 .. 2^24) rounds of four independent MFMAs with
  * no memory traffic: kind 0 = v_mfma_i32_32x32x32_i8 (65536 int8 ops each),
- * kind 1 = v_mfma_f32_16x16x32_f16 (16384 fp16 flops each).  Work per call =
+ * kind 1 = v_mfma_f32_16x16x32_f16 (16384 fp16 flops each), kind 2 =
+ * v_mfma_f32_32x32x16_f16 (32768 fp16 flops each); any other kind is
+ * QR_EINVAL.  Work per call =
  * waves * iters * 4 * (ops per MFMA).  `out` receives one checksum per lane
  * (so the loop cannot be removed), int32 [waves * 64], 4-byte aligned.
  */

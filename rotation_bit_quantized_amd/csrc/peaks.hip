@@ -8,22 +8,22 @@
 namespace qr {
 namespace {
 
-// Streaming copy: each lane moves 16-byte pieces with four loads in flight
+// Streaming copy: each lane moves 16-byte pieces with eight loads in flight
 // before its stores, nontemporal both ways, grid-strided over a persistent
-// grid (eight 256-thread blocks per CU).
-__global__ __launch_bounds__(256) void peak_copy_kernel(const v4u *__restrict__ src, v4u *__restrict__ dst,
-                                                         int64_t pieces) {
+// grid of one 1024-thread block per CU (the fastest of the block shapes and
+// depths tried: 256 to 1024 threads, one to four blocks per CU, four or
+// eight loads in flight).
+__global__ __launch_bounds__(1024) void peak_copy_kernel(const v4u *__restrict__ src, v4u *__restrict__ dst,
+                                                          int64_t pieces) {
+  constexpr int kDepth = 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < pieces; i += 4 * stride) {
-    const v4u a = __builtin_nontemporal_load(src + i);
-    const v4u b = __builtin_nontemporal_load(src + i + stride);
-    const v4u c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const v4u d = __builtin_nontemporal_load(src + i + 3 * stride);
-    __builtin_nontemporal_store(a, dst + i);
-    __builtin_nontemporal_store(b, dst + i + stride);
-    __builtin_nontemporal_store(c, dst + i + 2 * stride);
-    __builtin_nontemporal_store(d, dst + i + 3 * stride);
+  for (; i + (kDepth - 1) * stride < pieces; i += kDepth * stride) {
+    v4u v[kDepth];
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) v[j] = __builtin_nontemporal_load(src + i + j * stride);
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) __builtin_nontemporal_store(v[j], dst + i + j * stride);
   }
   for (; i < pieces; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
@@ -31,7 +31,9 @@ __global__ __launch_bounds__(256) void peak_copy_kernel(const v4u *__restrict__ 
 // Back-to-back MFMAs on four independent accumulators per wave (no memory
 // traffic in the loop); the sums are stored so that nothing is eliminated.
 // KIND 0: v_mfma_i32_32x32x32_i8 (65536 ops each); KIND 1:
-// v_mfma_f32_16x16x32_f16 (16384 flops each).
+// v_mfma_f32_16x16x32_f16 (16384 flops each); KIND 2: v_mfma_f32_32x32x16_f16
+// (32768 flops each).  The 16x16 fp16 shape issues at half the rate of the
+// 32x32 one, so the two bound kernels built on either shape.
 template <int KIND>
 __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, int *__restrict__ out) {
   const int lane = threadIdx.x & 63;
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, int *__restri
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
     out[wave * 64 + lane] = s;
-  } else {
+  } else if constexpr (KIND == 1) {
     v8h a, b;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -68,6 +70,24 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, int *__restri
 #pragma unroll
     for (int r = 0; r < 4; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
     out[wave * 64 + lane] = (int)f2u(s);
+  } else {
+    v8h a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a[j] = (_Float16)(0.001f * (lane + j));
+      b[j] = (_Float16)(0.002f * (iters - j));
+    }
+    v16f c0{}, c1{}, c2{}, c3{};
+    for (int it = 0; it < iters; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, b, c3, 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+    out[wave * 64 + lane] = (int)f2u(s);
   }
 }
 
@@ -83,26 +103,28 @@ qr_status qr_peak_copy(const void *src, void *dst, int64_t bytes, void *stream) 
   if (src == nullptr || dst == nullptr) return QR_EINVAL;
   if (((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return QR_EALIGN;
   const int64_t pieces = bytes / 16;
-  const int64_t want = (int64_t)qr::device_cu_count() * 8;
-  const int64_t need = (pieces + 255) / 256;
+  const int64_t want = (int64_t)qr::device_cu_count();
+  const int64_t need = (pieces + 1023) / 1024;
   const int64_t grid = need < want ? need : want;
-  qr::peak_copy_kernel<<<dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream>>>((const qr::v4u *)src,
-                                                                                      (qr::v4u *)dst, pieces);
+  qr::peak_copy_kernel<<<dim3((unsigned)grid), dim3(1024), 0, (hipStream_t)stream>>>((const qr::v4u *)src,
+                                                                                       (qr::v4u *)dst, pieces);
   return hipGetLastError() == hipSuccess ? QR_OK : QR_EDEVICE;
 }
 
 int64_t qr_peak_mfma_waves(void) { return (int64_t)qr::device_cu_count() * 8; }
 
 qr_status qr_peak_mfma(int64_t kind, int64_t iters, int32_t *out, void *stream) {
-  if (kind != 0 && kind != 1) return QR_EINVAL;
+  if (kind < 0 || kind > 2) return QR_EINVAL;
   if (iters <= 0 || iters > ((int64_t)1 << 24)) return QR_ESHAPE;
   if (out == nullptr) return QR_EINVAL;
   if ((uintptr_t)out & 3) return QR_EALIGN;
   const int64_t blocks = (int64_t)qr::device_cu_count() * 2;   // 8 waves per CU, two per SIMD
   if (kind == 0)
     qr::peak_mfma_kernel<0><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((int)iters, out);
-  else
+  else if (kind == 1)
     qr::peak_mfma_kernel<1><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((int)iters, out);
+  else
+    qr::peak_mfma_kernel<2><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((int)iters, out);
   return hipGetLastError() == hipSuccess ? QR_OK : QR_EDEVICE;
 }
 

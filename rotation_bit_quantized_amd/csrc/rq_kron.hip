@@ -31,7 +31,11 @@
 //    the four waves: the DMA of row r_{k+2} is issued during row r_k.  M-tile
 //    mt holds the rows i = 32 (mt >> 1) + 2 c + (mt & 1), c < 16: with the
 //    344-byte row pitch of m = 172, sixteen such rows start in sixteen
-//    distinct bank groups.
+//    distinct bank groups.  With a pitch of 8 mod 16 bytes every odd row
+//    starts half-way into a 16-byte unit, so each A-fragment is read as two
+//    8-byte halves: a 16-byte LDS read from such an address stalls the wave
+//    (at 131072 x 11008 the single-read form took about 1.4 ms, the split
+//    form about 1.3 ms).
 //  * The 64-point transform over i is in registers: i0, i5 are M-tile bits,
 //    i1, i2 register bits, i3, i4 lane bits 4, 5 brought into register bits
 //    with v_permlane16_swap / v_permlane32_swap.
@@ -175,8 +179,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron_kernel(
       for (int mp = 0; mp < kMT; mp += 2) {
         v8h acur[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          acur[u] = __builtin_bit_cast(v8h, *(const v4u *)(xbuf + a_off[mp + u] + 16 * g + 64 * ks));
+        for (int u = 0; u < 2; ++u) {
+          const uint8_t *pa = xbuf + a_off[mp + u] + 16 * g + 64 * ks;
+          const v2u lo = *(const v2u *)pa;
+          const v2u hi = *(const v2u *)(pa + 8);
+          acur[u] = __builtin_bit_cast(v8h, v4u{lo[0], lo[1], hi[0], hi[1]});
+        }
 #pragma unroll
         for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
