@@ -103,7 +103,7 @@ def source_hash(files):
 CSRC = "rotation_bit_quantized_amd/csrc/"
 KERNEL_SOURCES = {
     "gemm_prefill_kernel": [CSRC + "gemm_prefill.hip", CSRC + "qr_common.h"],
-    "gemm_decode_kernel": [CSRC + "gemm_decode.hip", CSRC + "qr_common.h"],
+    "gemm_decode_lds_kernel": [CSRC + "gemm_decode.hip", CSRC + "qr_common.h"],
     "rq_kron_kernel": [CSRC + "rq_kron.hip", CSRC + "qr_common.h"],
     "rq_pow2_kernel": [CSRC + "rq_pow2.hip", CSRC + "qr_common.h"],
 }
@@ -153,12 +153,14 @@ def measure_peaks(dev):
     copy_ms, _ = time_each(lambda i: qr.peak_copy(src, dst), 5, st, warm=1)
     del src, dst
     out = {"hbm_copy_GBs": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1)}
-    for kind, key in ((0, "mfma_int8_TOPS"), (1, "mfma_fp16_16x16_TFLOPS"), (2, "mfma_fp16_32x32_TFLOPS")):
+    for kind, key in ((0, "mfma_int8_TOPS"), (3, "mfma_int8_16x16_TOPS"), (1, "mfma_fp16_16x16_TFLOPS"),
+                      (2, "mfma_fp16_32x32_TFLOPS")):
         buf, ops = qr.peak_mfma(kind, 20000)
         ms, _ = time_each(lambda i: qr.peak_mfma(kind, 20000, buf), 5, st, warm=1)
         out[key] = round(ops / (ms * 1e-3) / 1e12, 1)
     out["how"] = ("qr_peak_copy of 1 GiB (2 GiB moved); qr_peak_mfma: 8 waves per CU, four independent "
-                  "v_mfma_i32_32x32x32_i8 / v_mfma_f32_16x16x32_f16 / v_mfma_f32_32x32x16_f16 chains, "
+                  "v_mfma_i32_32x32x32_i8 / v_mfma_i32_16x16x64_i8 / v_mfma_f32_16x16x32_f16 / v_mfma_f32_32x32x16_f16 "
+                  "chains, "
                   "20000 rounds; medians of 5")
     return out
 
@@ -222,7 +224,7 @@ def ingest_pmc(cfg_name, fetch_dir, write_dir, calib_mib):
     import csv
     import glob
     import re
-    gemm = "gemm_decode_kernel" if cfg_name == "c5" else "gemm_prefill_kernel"
+    gemm = "gemm_decode_lds_kernel" if cfg_name == "c5" else "gemm_prefill_kernel"
     cfg = None
     try:
         import workloads as W
@@ -456,7 +458,7 @@ def run_step(args):
                          "us_median": round(rq_ms * 1e3, 3), "us_mean": round(rq_mean * 1e3, 3),
                          "GB/s": round(rq_gbs, 1), **frac(rq_gbs, HBM_PEAK_GBS, "hbm_copy_GBs"),
                          "bytes": rq_bytes},
-        "int4_gemm": {"kernel": "gemm_decode_kernel" if M <= 64 else "gemm_prefill_kernel",
+        "int4_gemm": {"kernel": "gemm_decode_lds_kernel" if M <= 64 else "gemm_prefill_kernel",
                       "us_median": round(gemm_ms * 1e3, 3), "us_mean": round(gemm_mean * 1e3, 3),
                       "TOPS": round(gemm_tops, 2), **frac(gemm_tops, INT8_PEAK_TOPS, "mfma_int8_TOPS"),
                       "GB/s": round(gemm_gbs, 1), "frac_hbm": round(gemm_gbs / HBM_PEAK_GBS, 4),
@@ -475,8 +477,8 @@ def run_step(args):
 
     # the dominant kernel of the step and its roofline
     if M <= 64:   # decode: the GEMM streams the weights, HBM-bound
-        traffic = load_traffic(f"int4_gemm_{cfg.name}", "gemm_decode_kernel", gemm_bytes)
-        roofline = {"bound": "hbm", "kernel": "int4_gemm (gemm_decode_kernel)", "achieved": round(gemm_gbs, 1),
+        traffic = load_traffic(f"int4_gemm_{cfg.name}", "gemm_decode_lds_kernel", gemm_bytes)
+        roofline = {"bound": "hbm", "kernel": "int4_gemm (gemm_decode_lds_kernel)", "achieved": round(gemm_gbs, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4)}
     else:
         traffic = load_traffic(f"int4_gemm_{cfg.name}", "gemm_prefill_kernel", gemm_bytes)

@@ -34,7 +34,8 @@ int64_t qr_peak_mfma_waves(void);
  * Every wave issues `iters` (1 .. 2^24) rounds of four independent MFMAs with
  * no memory traffic: kind 0 = v_mfma_i32_32x32x32_i8 (65536 int8 ops each),
  * kind 1 = v_mfma_f32_16x16x32_f16 (16384 fp16 flops each), kind 2 =
- * v_mfma_f32_32x32x16_f16 (32768 fp16 flops each); any other kind is
+ * v_mfma_f32_32x32x16_f16 (32768 fp16 flops each), kind 3 =
+ * v_mfma_i32_16x16x64_i8 (32768 int8 ops each); any other kind is
  * QR_EINVAL.  Work per call =
  * waves * iters * 4 * (ops per MFMA).  `out` receives one checksum per lane
  * (so the loop cannot be removed), int32 [waves * 64], 4-byte aligned.

@@ -495,12 +495,12 @@ def peak_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
 
 def peak_mfma(kind: int, iters: int, out=None, stream=None):
     """qr_peak_mfma: kind 0 = int8 32x32x32, 1 = fp16 16x16x32, 2 = fp16
-    32x32x16.  Returns (out, ops per call)."""
+    32x32x16, 3 = int8 16x16x64.  Returns (out, ops per call)."""
     waves = int(library().qr_peak_mfma_waves())
     if out is None:
         out = torch.empty((waves * 64,), dtype=torch.int32, device="cuda")
     _need(out, torch.int32, "out", (waves * 64,), True)
     _on_gpu(out=out)
     _check("qr_peak_mfma", library().qr_peak_mfma(int(kind), int(iters), _ptr(out), _stream(stream)))
-    per = {0: 65536, 1: 16384, 2: 32768}[int(kind)]
+    per = {0: 65536, 1: 16384, 2: 32768, 3: 32768}[int(kind)]
     return out, waves * int(iters) * 4 * per

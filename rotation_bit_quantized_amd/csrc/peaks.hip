@@ -32,8 +32,8 @@ __global__ __launch_bounds__(1024) void peak_copy_kernel(const v4u *__restrict__
 // traffic in the loop); the sums are stored so that nothing is eliminated.
 // KIND 0: v_mfma_i32_32x32x32_i8 (65536 ops each); KIND 1:
 // v_mfma_f32_16x16x32_f16 (16384 flops each); KIND 2: v_mfma_f32_32x32x16_f16
-// (32768 flops each).  The 16x16 fp16 shape issues at half the rate of the
-// 32x32 one, so the two bound kernels built on either shape.
+// (32768 flops each); KIND 3: v_mfma_i32_16x16x64_i8 (32768 ops each).  The
+// 16x16 shapes and the 32x32 ones bound the kernels built on them.
 template <int KIND>
 __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, int *__restrict__ out) {
   const int lane = threadIdx.x & 63;
@@ -70,6 +70,20 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, int *__restri
 #pragma unroll
     for (int r = 0; r < 4; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
     out[wave * 64 + lane] = (int)f2u(s);
+  } else if constexpr (KIND == 3) {
+    const v4i a = {lane, lane + 1, lane + 2, lane + 3};
+    const v4i b = {iters, lane, 3, 5};
+    v4i c0{}, c1{}, c2{}, c3{};
+    for (int it = 0; it < iters; ++it) {
+      c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, a, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, b, c3, 0, 0, 0);
+    }
+    int s = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+    out[wave * 64 + lane] = s;
   } else {
     v8h a, b;
 #pragma unroll
@@ -114,7 +128,7 @@ qr_status qr_peak_copy(const void *src, void *dst, int64_t bytes, void *stream) 
 int64_t qr_peak_mfma_waves(void) { return (int64_t)qr::device_cu_count() * 8; }
 
 qr_status qr_peak_mfma(int64_t kind, int64_t iters, int32_t *out, void *stream) {
-  if (kind < 0 || kind > 2) return QR_EINVAL;
+  if (kind < 0 || kind > 3) return QR_EINVAL;
   if (iters <= 0 || iters > ((int64_t)1 << 24)) return QR_ESHAPE;
   if (out == nullptr) return QR_EINVAL;
   if ((uintptr_t)out & 3) return QR_EALIGN;
@@ -123,8 +137,10 @@ qr_status qr_peak_mfma(int64_t kind, int64_t iters, int32_t *out, void *stream) 
     qr::peak_mfma_kernel<0><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((int)iters, out);
   else if (kind == 1)
     qr::peak_mfma_kernel<1><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((int)iters, out);
-  else
+  else if (kind == 2)
     qr::peak_mfma_kernel<2><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((int)iters, out);
+  else
+    qr::peak_mfma_kernel<3><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((int)iters, out);
   return hipGetLastError() == hipSuccess ? QR_OK : QR_EDEVICE;
 }
 

@@ -35,7 +35,7 @@ def test_peak_probes_reject_bad_arguments():
     assert lib.qr_peak_copy(MIS, A16, 1024, None) == qr.QR_EALIGN
     assert lib.qr_peak_copy(None, A16, 1024, None) == qr.QR_EINVAL
     assert lib.qr_peak_copy(None, None, 0, None) == qr.QR_OK
-    assert lib.qr_peak_mfma(3, 10, A16, None) == qr.QR_EINVAL
+    assert lib.qr_peak_mfma(4, 10, A16, None) == qr.QR_EINVAL
     assert lib.qr_peak_mfma(-1, 10, A16, None) == qr.QR_EINVAL
     assert lib.qr_peak_mfma(0, 0, A16, None) == qr.QR_ESHAPE
     assert lib.qr_peak_mfma(0, 10, None, None) == qr.QR_EINVAL

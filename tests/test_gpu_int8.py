@@ -57,7 +57,8 @@ def test_int8_gemm_i32_exact(qr, M, N, K, group):
 
 
 @pytest.mark.parametrize("M,N,K,group", [(64, 512, 512, 0), (320, 640, 4096, 0), (257, 130, 1024, 128),
-                                         (40, 300, 1024, 128), (130, 96, 11008, 0)])
+                                         (40, 300, 1024, 128), (130, 96, 11008, 0), (17, 100, 4096, 0),
+                                         (33, 4100, 11008, 0)])
 def test_int8_gemm_epilogue(qr, M, N, K, group):
     rng = np.random.default_rng(M + N)
     qa = W.make_random_codes(M, K, seed=M, lo=-127, hi=127)

@@ -280,7 +280,8 @@ def test_gemm_i32_exact_on_oracle_codes_c1(qr):
 
 @pytest.mark.parametrize("M,N,K,group", [(64, 512, 512, 0), (320, 640, 4096, 0), (257, 130, 1024, 128),
                                          (40, 300, 1024, 128), (130, 96, 11008, 0), (130, 96, 384, 0),
-                                         (257, 130, 640, 128), (150, 160, 1152, 384)])
+                                         (257, 130, 640, 128), (150, 160, 1152, 384),
+                                         (17, 100, 4096, 0), (33, 4100, 11008, 0), (1, 40, 128, 0)])
 def test_gemm_epilogue_on_given_codes(qr, M, N, K, group):
     rng = np.random.default_rng(M * N)
     qa = W.make_random_codes(M, K, seed=M)
@@ -310,7 +311,8 @@ def test_gemm_padded_output(qr):
     check_output(yb[:, :70], O.dequantize_output(O.int_gemm(qa, qw), sa, sw))
 
 
-@pytest.mark.parametrize("M,N,K,group", [(130, 70, 512, 0), (200, 200, 640, 128), (300, 389, 1024, 0)])
+@pytest.mark.parametrize("M,N,K,group", [(130, 70, 512, 0), (200, 200, 640, 128), (300, 389, 1024, 0),
+                                         (17, 70, 512, 0), (40, 389, 2048, 0)])
 def test_gemm_unaligned_output(qr, M, N, K, group):
     """y 2-byte aligned only and a row pitch that is not a multiple of 8:
     the epilogue's element-wise store path."""
