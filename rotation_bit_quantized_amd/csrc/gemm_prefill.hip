@@ -124,8 +124,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   static_assert(WAVE_LOADS * (STAGES - 1) < 64, "vmcnt range");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES + SCALE_SLOTS * SCALE_BYTES];
+  // Per-channel fp16 output: the tile's output scales (s_x of the BM rows,
+  // then s_w of the BN columns) travel by DMA into LDS at the start, so that
+  // the epilogue does not wait a memory round trip for them; only where the
+  // 4 bytes per row still let the CU hold as many blocks.
+  constexpr int BLOCKS_PER_CU = OCC * 4 / NW;
+  constexpr bool OSC = !GROUPED && !OUT_I32 &&
+                       (STAGES * STAGE_BYTES + ROWS * 4) * BLOCKS_PER_CU <= 160 * 1024;
+  constexpr int OSC_INST = OSC ? ROWS / 64 : 0;   // 4-byte DMA wave-instructions
+  static_assert(!OSC || (ROWS % 64 == 0 && OSC_INST <= NW), "output scale DMA split");
+  __shared__ __attribute__((aligned(1024))) uint8_t
+      smem[STAGES * STAGE_BYTES + SCALE_SLOTS * SCALE_BYTES + (OSC ? ROWS * 4 : 0)];
   uint8_t *const scale_ring = smem + STAGES * STAGE_BYTES;
+  const float *const osc = (const float *)(smem + STAGES * STAGE_BYTES + SCALE_SLOTS * SCALE_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -452,6 +463,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
     }
   };
 
+  if constexpr (OSC) {
+    // issued before the stages: the first tile wait below covers them too
+    if (wave < OSC_INST) {
+      const int e = 64 * wave + lane;
+      const float *p = e < BM ? sa + min(m0 + e, M - 1) : sw + min(n0 + e - BM, N - 1);
+      __builtin_amdgcn_global_load_lds((const void *)p, (lds_void *)(osc + 64 * wave), 4, 0, 0);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
     if (s < KT) issue(s, s);
@@ -489,20 +508,36 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
         }
       }
   } else if constexpr (!OUT_I32) {
-    // fp16 output, staged through LDS: each wave writes its WM x WN tile
-    // row-major into a private region of the (now idle) stage buffers, then
-    // stores whole 16-byte row pieces (2-byte stores straight from the
-    // fragment layout, one column per lane, would take 8x the store
-    // instructions and stall the CU's two blocks together).
+    // fp16 output, staged through LDS: each wave writes 32 rows of its
+    // WM x WN tile at a time row-major into a private region of an idle stage
+    // buffer, reads them back and stores whole 16-byte row pieces (2-byte
+    // stores straight from the fragment layout, one column per lane, would
+    // take 8x the store instructions).  The buffer is the one that held
+    // K-tile KT - 2 (or the unused one when KT == 1): every wave has passed
+    // that tile's refill barrier and no DMA targets it any more, so no wave
+    // waits for the others here.
     constexpr int PITCH = WN * 2 + 16;   // bytes per LDS row; the pad spreads the two half-waves' banks
-    static_assert(NW * WM * PITCH <= STAGES * STAGE_BYTES, "epilogue staging must fit in the stage buffers");
-    static_assert((WM * (WN / 8)) % 64 == 0, "whole wave passes over the output pieces");
+    constexpr int HROWS = 32;            // rows staged at a time: one fragment row
+    static_assert(NW * HROWS * PITCH <= STAGE_BYTES, "epilogue staging must fit in one stage buffer");
+    static_assert((HROWS * (WN / 8)) % 64 == 0, "whole wave passes over the output pieces");
+    static_assert(STAGES == 2, "the idle stage buffer is the other one");
     unsigned short *y = (unsigned short *)out;
-    // Output scales: every load issued at once from clamped (always valid)
-    // indices, before the barrier, so that one memory latency covers them;
+    // Output scales: from LDS (OSC), or every load issued at once from
+    // clamped (always valid) indices so that one memory latency covers them;
     // rows or columns past the edge are never stored.
     float swv[FN], sav[GROUPED ? 1 : FM][16];
-    if constexpr (!GROUPED) {
+    if constexpr (OSC) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) swv[j] = osc[BM + wn * WN + j * 32 + lcol] * UNSCALE;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const v4f v = *(const v4f *)(osc + wm * WM + i * 32 + 8 * r4 + lrow);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sav[i][4 * r4 + r] = v[r];
+        }
+    } else if constexpr (!GROUPED) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) swv[j] = sw[min(n0 + wn * WN + j * 32 + lcol, N - 1)] * UNSCALE;
 #pragma unroll
@@ -510,14 +545,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
 #pragma unroll
         for (int r = 0; r < 16; ++r) sav[i][r] = sa[min(m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3), M - 1)];
     }
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();   // every wave is done reading the stage buffers
-    uint8_t *ot = smem + wave * WM * PITCH;
+    uint8_t *ot = smem + (KT % STAGES) * STAGE_BYTES + wave * HROWS * PITCH;
+    const bool vec_ok = ((uintptr_t)y % 16 == 0) && (ld_y % 8 == 0);
+    constexpr int PIECES = WN / 8;   // 16-byte pieces per row
+    constexpr int PASSES = HROWS * PIECES / 64;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int trow = i * 32 + 8 * (r >> 2) + lrow + (r & 3);   // row within the wave tile
+        const int trow = 8 * (r >> 2) + lrow + (r & 3);   // row within the 32 staged rows
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           float val;
@@ -528,32 +564,30 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
           *(unsigned short *)(ot + trow * PITCH + (j * 32 + lcol) * 2) = float_to_half_bits(val);
         }
       }
-    // the wave reads back only what it wrote itself: LDS operations of one
-    // wave complete in order, no barrier needed
-    const bool vec_ok = ((uintptr_t)y % 16 == 0) && (ld_y % 8 == 0);
-    constexpr int PIECES = WN / 8;   // 16-byte pieces per row
-    constexpr int PASSES = WM * PIECES / 64;
-    v4u pv[PASSES];   // all reads first, then the (edge-guarded) stores
+      // the wave reads back only what it wrote itself: LDS operations of one
+      // wave complete in order, no barrier needed
+      v4u pv[PASSES];   // all reads first, then the (edge-guarded) stores
 #pragma unroll
-    for (int it = 0; it < PASSES; ++it) {
-      const int p = it * 64 + lane;
-      pv[it] = *(const v4u *)(ot + (p / PIECES) * PITCH + (p % PIECES) * 16);
-    }
+      for (int it = 0; it < PASSES; ++it) {
+        const int p = it * 64 + lane;
+        pv[it] = *(const v4u *)(ot + (p / PIECES) * PITCH + (p % PIECES) * 16);
+      }
 #pragma unroll
-    for (int it = 0; it < PASSES; ++it) {
-      const int p = it * 64 + lane;
-      const int trow = p / PIECES, cp = p % PIECES;
-      const int row = m0 + wm * WM + trow;
-      const int col = n0 + wn * WN + cp * 8;
-      const v4u v = pv[it];
-      if (row < M) {
-        unsigned short *dst = y + (int64_t)row * ld_y + col;
-        if (vec_ok && col + 8 <= N) {
-          *(v4u *)dst = v;
-        } else {
+      for (int it = 0; it < PASSES; ++it) {
+        const int p = it * 64 + lane;
+        const int trow = p / PIECES, cp = p % PIECES;
+        const int row = m0 + wm * WM + i * HROWS + trow;
+        const int col = n0 + wn * WN + cp * 8;
+        const v4u v = pv[it];
+        if (row < M) {
+          unsigned short *dst = y + (int64_t)row * ld_y + col;
+          if (vec_ok && col + 8 <= N) {
+            *(v4u *)dst = v;
+          } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (col + e < N) dst[e] = (unsigned short)(v[e >> 1] >> (16 * (e & 1)));
+            for (int e = 0; e < 8; ++e)
+              if (col + e < N) dst[e] = (unsigned short)(v[e >> 1] >> (16 * (e & 1)));
+          }
         }
       }
     }
