@@ -86,6 +86,8 @@ __device__ __forceinline__ void tile_of(int bid, int tm_count, int tn_count, int
   tn = in_band / gm;
 }
 
+constexpr bool persistent_shape(int bm, bool grouped) { return bm == 256 && !grouped; }
+
 // OCC waves per SIMD: blocks of 4 waves run OCC to a CU, blocks of 8 waves
 // OCC/2.  At OCC 1 a wave has the whole register file (AGPR accumulators).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool GROUPED, bool OUT_I32, bool SHORT_TAIL,
@@ -129,14 +131,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   // the epilogue does not wait a memory round trip for them; only where the
   // 4 bytes per row still let the CU hold as many blocks.
   constexpr int BLOCKS_PER_CU = OCC * 4 / NW;
+  // Persistent blocks for the 256-row shape with per-channel scales; the
+  // others keep one block per tile (a loop over tiles would push them past
+  // the register file).
+  constexpr bool PERSIST = persistent_shape(BM, GROUPED);
+  // Two slots, so that the next tile's scales can arrive during this
+  // tile's epilogue.
   constexpr bool OSC = !GROUPED && !OUT_I32 &&
-                       (STAGES * STAGE_BYTES + ROWS * 4) * BLOCKS_PER_CU <= 160 * 1024;
+                       (STAGES * STAGE_BYTES + 2 * ROWS * 4) * BLOCKS_PER_CU <= 160 * 1024;
   constexpr int OSC_INST = OSC ? ROWS / 64 : 0;   // 4-byte DMA wave-instructions
   static_assert(!OSC || (ROWS % 64 == 0 && OSC_INST <= NW), "output scale DMA split");
   __shared__ __attribute__((aligned(1024))) uint8_t
-      smem[STAGES * STAGE_BYTES + SCALE_SLOTS * SCALE_BYTES + (OSC ? ROWS * 4 : 0)];
+      smem[STAGES * STAGE_BYTES + SCALE_SLOTS * SCALE_BYTES + (OSC ? 2 * ROWS * 4 : 0)];
   uint8_t *const scale_ring = smem + STAGES * STAGE_BYTES;
-  const float *const osc = (const float *)(smem + STAGES * STAGE_BYTES + SCALE_SLOTS * SCALE_BYTES);
+  float *const osc_base = (float *)(smem + STAGES * STAGE_BYTES + SCALE_SLOTS * SCALE_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -146,9 +154,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int tm_count = (M + BM - 1) / BM;
   const int tn_count = (N + BN - 1) / BN;
-  int tm, tn;
-  tile_of(blockIdx.x, tm_count, tn_count, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int tiles = tm_count * tn_count;
   const int64_t kbytes = (int64_t)K * CB / 8;
   const int KT = (K + kBK - 1) / kBK;
   // SHORT_TAIL: K is an odd multiple of 128, the last K-tile holds 128 codes
@@ -160,16 +166,31 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   // the matrix edge re-read the last row; their results are never stored.
   // Whether an instruction reads A or W is uniform; the per-lane part is a
   // 32-bit offset from the block's first row.
-  const uint8_t *a_base = A + (int64_t)m0 * kbytes;
-  const uint8_t *w_base = W + (int64_t)n0 * kbytes;
+  // The DMA state describes the tile whose K-tiles the DMA instructions
+  // fetch: the current one during its K loop, the next one from the end of
+  // the K loop on (its first two K-tiles and output scales arrive during the
+  // current tile's epilogue).  m0, n0 stay the current tile's.
+  int dm0, dn0;
+  const uint8_t *a_base, *w_base;
   uint32_t src_off[LOADS];
+  auto set_dma_tile = [&](int bid) __attribute__((always_inline)) {
+    int tm, tn;
+    tile_of(bid, tm_count, tn_count, tm, tn);
+    dm0 = tm * BM;
+    dn0 = tn * BN;
+    a_base = A + (int64_t)dm0 * kbytes;
+    w_base = W + (int64_t)dn0 * kbytes;
 #pragma unroll
-  for (int q = 0; q < LOADS; ++q) {
-    const int trow = 8 * (NW * q + wave) + (lane >> 3);   // 0 .. ROWS-1
-    const int piece = swz(trow, lane & 7);
-    const int rel = trow < BM ? min(trow, M - 1 - m0) : min(trow - BM, N - 1 - n0);
-    src_off[q] = (uint32_t)rel * (uint32_t)kbytes + (uint32_t)(piece * 16);
-  }
+    for (int q = 0; q < LOADS; ++q) {
+      const int trow = 8 * (NW * q + wave) + (lane >> 3);   // 0 .. ROWS-1
+      const int piece = swz(trow, lane & 7);
+      const int rel = trow < BM ? min(trow, M - 1 - dm0) : min(trow - BM, N - 1 - dn0);
+      src_off[q] = (uint32_t)rel * (uint32_t)kbytes + (uint32_t)(piece * 16);
+    }
+  };
+  int bid = blockIdx.x;
+  set_dma_tile(bid);
+  int m0 = dm0, n0 = dn0;
   // Whether this lane's global piece lies in the upper half of the row
   // (piece >= 4): with trow = 8 X + (lane >> 3), (trow >> 1) & 7 equals
   // 4 (X & 1) + (lane >> 4), and X = NW q + wave has the parity of wave, so
@@ -195,8 +216,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
           const int h = e >= ROWS;
           const int ee = e - h * ROWS;
           const int gidx = min((kt * kBK + h * kHalfCodes) / group, G - 1);
-          const float *p = ee < BM ? sa + (int64_t)min(m0 + ee, M - 1) * G + gidx
-                                   : sw + (int64_t)min(n0 + ee - BM, N - 1) * G + gidx;
+          const float *p = ee < BM ? sa + (int64_t)min(dm0 + ee, M - 1) * G + gidx
+                                   : sw + (int64_t)min(dn0 + ee - BM, N - 1) * G + gidx;
           __builtin_amdgcn_global_load_lds((const void *)p,
                                            (lds_void *)(scale_ring + (kt % 3) * SCALE_BYTES +
                                                         256 * (NW * qs + wave)),
@@ -209,25 +230,36 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) issue_q(kt, stage, q);
   };
+  // the DMA tile's output scales into slot `slot` (before its K-tiles, so
+  // that the wait for its first K-tile covers them)
+  auto issue_osc = [&](int slot) __attribute__((always_inline)) {
+    if constexpr (OSC) {
+      if (wave < OSC_INST) {
+        const int e = 64 * wave + lane;
+        const float *p = e < BM ? sa + min(dm0 + e, M - 1) : sw + min(dn0 + e - BM, N - 1);
+        __builtin_amdgcn_global_load_lds((const void *)p, (lds_void *)(osc_base + slot * ROWS + 64 * wave), 4, 0,
+                                         0);
+      }
+    }
+  };
 
   v16i acc[FM][FN];
   v16f facc[GROUPED ? FM : 1][GROUPED ? FN : 1];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
-  if constexpr (GROUPED) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) facc[i][j] = v16f{};
-  }
 
-  const int lrow = 4 * (lane >> 5);   // output row offset within a fragment: + 8*(r/4) + r%4
-  const int lcol = lane & 31;
-  const int ra = wm * WM + (lane & 31);            // tile row of this lane in A fragment 0
-  const int rb = BM + wn * WN + (lane & 31);       // tile row of this lane in W fragment 0
-  const int half = lane >> 5;                      // which 16-byte piece of a 32-byte chunk
+  // Lane-dependent offsets, set again at the start of every tile from an
+  // opaque copy of the lane index: otherwise the compiler hoists everything
+  // derived from them (every LDS and output address of the epilogue) out of
+  // the tile loop and keeps it live through the K loop, which spills.
+  int lrow, lcol, ra, rb, half;
+  auto set_lane_offsets = [&]() __attribute__((always_inline)) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    lrow = 4 * (l >> 5);            // output row offset within a fragment: + 8*(r/4) + r%4
+    lcol = l & 31;
+    ra = wm * WM + (l & 31);        // tile row of this lane in A fragment 0
+    rb = BM + wn * WN + (l & 31);   // tile row of this lane in W fragment 0
+    half = l >> 5;                  // which 16-byte piece of a 32-byte chunk
+  };
 
   // Chunk pipeline registers: the raw codes of two chunks (LDS -> VGPR, one
   // read in flight while the other is widened) and the widened operands of
@@ -463,134 +495,183 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
     }
   };
 
-  if constexpr (OSC) {
-    // issued before the stages: the first tile wait below covers them too
-    if (wave < OSC_INST) {
-      const int e = 64 * wave + lane;
-      const float *p = e < BM ? sa + min(m0 + e, M - 1) : sw + min(n0 + e - BM, N - 1);
-      __builtin_amdgcn_global_load_lds((const void *)p, (lds_void *)(osc + 64 * wave), 4, 0, 0);
-    }
-  }
+  // Persistent blocks (PERSIST): block b takes the tiles b, b + gridDim.x,
+  // ... (the grid is a multiple of 8, so every tile keeps the XCD that
+  // tile_of gave it).  The first tile's scales and K-tiles 0, 1 go out here;
+  // each later tile's during its predecessor's epilogue.  Otherwise one
+  // block per tile.
+  issue_osc(0);
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
     if (s < KT) issue(s, s);
-  wait_tile(min(STAGES - 1, KT - 1));
-  __builtin_amdgcn_s_barrier();
-  read_raw(smem, 0, 0);
-  wait_lgkm0();
-  widen_into(0, 0);
-  read_raw(smem, 1, 1);
-  __builtin_amdgcn_sched_barrier(0);
 
-  // Tiles followed by another (refilling their buffer while one remains),
-  // then the last tile, peeled.
-  int kt = 0;
-  for (; kt + STAGES < KT; ++kt) tile(kt, std::integral_constant<int, kNext>{});
-  for (; kt + 1 < KT; ++kt) tile(kt, std::integral_constant<int, kNextNoDma>{});
-  if constexpr (SHORT_TAIL)
-    tile(KT - 1, std::integral_constant<int, kLastShort>{});
-  else
-    tile(KT - 1, std::integral_constant<int, kLastFull>{});
-  __builtin_amdgcn_sched_barrier(0);   // keep the epilogue out of the last MFMAs
+  for (int iter = 0;; ++iter) {
+    const int nbid = bid + (int)gridDim.x;
+    const bool has_next = PERSIST && nbid < tiles;   // uniform over the block
+    set_lane_offsets();
 
-  // ---- epilogue
-  if constexpr (OUT_I32 && !GROUPED) {
-    int32_t *o = (int32_t *)out;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * WN + j * 32 + lcol;
+      for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) facc[i][j] = v16f{};
+    }
+
+    // K-tile 0 has landed (for a later tile: issued after it are K-tile 1
+    // and the previous tile's output stores, so waiting until at most one
+    // stage's DMA count is outstanding implies it, loads returning in order)
+    wait_tile(min(STAGES - 1, KT - 1));
+    __builtin_amdgcn_s_barrier();
+    read_raw(smem, 0, 0);
+    wait_lgkm0();
+    widen_into(0, 0);
+    read_raw(smem, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Tiles followed by another (refilling their buffer while one remains),
+    // then the last tile, peeled.
+    int kt = 0;
+    for (; kt + STAGES < KT; ++kt) tile(kt, std::integral_constant<int, kNext>{});
+    for (; kt + 1 < KT; ++kt) tile(kt, std::integral_constant<int, kNextNoDma>{});
+    if constexpr (SHORT_TAIL)
+      tile(KT - 1, std::integral_constant<int, kLastShort>{});
+    else
+      tile(KT - 1, std::integral_constant<int, kLastFull>{});
+    __builtin_amdgcn_sched_barrier(0);   // keep the epilogue out of the last MFMAs
+
+    // every wave is done with the stage buffers and the scale ring
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+
+    // ---- epilogue, with the next tile's first K-tiles on their way
+    if constexpr (OUT_I32) {
+      if (has_next) {
+        set_dma_tile(nbid);
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s)
+          if (s < KT) issue(s, s);
+      }
+      if constexpr (!GROUPED) {
+        int32_t *o = (int32_t *)out;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * WN + j * 32 + lcol;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
+              if (row < M && col < N) o[(int64_t)row * N + col] = acc[i][j][r] >> SHIFT;
+            }
+          }
+      }
+    } else {
+      // fp16 output, staged through LDS: each wave writes 32 rows of its
+      // WM x WN tile at a time row-major into a private region of stage
+      // buffer 1, reads them back and stores whole 16-byte row pieces
+      // (2-byte stores straight from the fragment layout, one column per
+      // lane, would take 8x the store instructions).  The next tile's K-tile
+      // 0 goes into buffer 0 at once, its K-tile 1 into buffer 1 after the
+      // staging.
+      constexpr int PITCH = WN * 2 + 16;   // bytes per LDS row; the pad spreads the two half-waves' banks
+      constexpr int HROWS = 32;            // rows staged at a time: one fragment row
+      static_assert(NW * HROWS * PITCH <= STAGE_BYTES, "epilogue staging must fit in one stage buffer");
+      static_assert((HROWS * (WN / 8)) % 64 == 0, "whole wave passes over the output pieces");
+      static_assert(STAGES == 2, "staging in buffer 1 while buffer 0 takes the next tile");
+      unsigned short *y = (unsigned short *)out;
+      // Output scales: from LDS (OSC), or every load issued at once from
+      // clamped (always valid) indices so that one memory latency covers
+      // them; rows or columns past the edge are never stored.
+      float swv[FN], sav[GROUPED ? 1 : FM][16];
+      if constexpr (OSC) {
+        const float *osc = osc_base + (iter & 1) * ROWS;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) swv[j] = osc[BM + wn * WN + j * 32 + lcol] * UNSCALE;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const v4f v = *(const v4f *)(osc + wm * WM + i * 32 + 8 * r4 + lrow);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sav[i][4 * r4 + r] = v[r];
+          }
+      } else if constexpr (!GROUPED) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) swv[j] = sw[min(n0 + wn * WN + j * 32 + lcol, N - 1)] * UNSCALE;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sav[i][r] = sa[min(m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3), M - 1)];
+      }
+      if (has_next) {
+        set_dma_tile(nbid);
+        issue_osc((iter + 1) & 1);
+        issue(0, 0);
+      }
+      uint8_t *ot = smem + STAGE_BYTES + wave * HROWS * PITCH;
+      constexpr int PIECES = WN / 8;   // 16-byte pieces per row
+      constexpr int PASSES = HROWS * PIECES / 64;
+      const bool vec_ok = ((uintptr_t)y % 16 == 0) && (ld_y % 8 == 0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3);
-          if (row < M && col < N) o[(int64_t)row * N + col] = acc[i][j][r] >> SHIFT;
+          const int trow = 8 * (r >> 2) + lrow + (r & 3);   // row within the 32 staged rows
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            float val;
+            if constexpr (GROUPED)
+              val = facc[i][j][r];
+            else
+              val = (float)acc[i][j][r] * (sav[i][r] * swv[j]);
+            *(unsigned short *)(ot + trow * PITCH + (j * 32 + lcol) * 2) = float_to_half_bits(val);
+          }
         }
-      }
-  } else if constexpr (!OUT_I32) {
-    // fp16 output, staged through LDS: each wave writes 32 rows of its
-    // WM x WN tile at a time row-major into a private region of an idle stage
-    // buffer, reads them back and stores whole 16-byte row pieces (2-byte
-    // stores straight from the fragment layout, one column per lane, would
-    // take 8x the store instructions).  The buffer is the one that held
-    // K-tile KT - 2 (or the unused one when KT == 1): every wave has passed
-    // that tile's refill barrier and no DMA targets it any more, so no wave
-    // waits for the others here.
-    constexpr int PITCH = WN * 2 + 16;   // bytes per LDS row; the pad spreads the two half-waves' banks
-    constexpr int HROWS = 32;            // rows staged at a time: one fragment row
-    static_assert(NW * HROWS * PITCH <= STAGE_BYTES, "epilogue staging must fit in one stage buffer");
-    static_assert((HROWS * (WN / 8)) % 64 == 0, "whole wave passes over the output pieces");
-    static_assert(STAGES == 2, "the idle stage buffer is the other one");
-    unsigned short *y = (unsigned short *)out;
-    // Output scales: from LDS (OSC), or every load issued at once from
-    // clamped (always valid) indices so that one memory latency covers them;
-    // rows or columns past the edge are never stored.
-    float swv[FN], sav[GROUPED ? 1 : FM][16];
-    if constexpr (OSC) {
+        // the wave reads back only what it wrote itself (LDS operations of
+        // one wave complete in order), before it overwrites the region
+        v4u pv[PASSES];   // all reads first, then the (edge-guarded) stores
 #pragma unroll
-      for (int j = 0; j < FN; ++j) swv[j] = osc[BM + wn * WN + j * 32 + lcol] * UNSCALE;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const v4f v = *(const v4f *)(osc + wm * WM + i * 32 + 8 * r4 + lrow);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sav[i][4 * r4 + r] = v[r];
+        for (int it = 0; it < PASSES; ++it) {
+          const int p = it * 64 + lane;
+          pv[it] = *(const v4u *)(ot + (p / PIECES) * PITCH + (p % PIECES) * 16);
         }
-    } else if constexpr (!GROUPED) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) swv[j] = sw[min(n0 + wn * WN + j * 32 + lcol, N - 1)] * UNSCALE;
+        for (int it = 0; it < PASSES; ++it) {
+          const int p = it * 64 + lane;
+          const int trow = p / PIECES, cp = p % PIECES;
+          const int row = m0 + wm * WM + i * HROWS + trow;
+          const int col = n0 + wn * WN + cp * 8;
+          const v4u v = pv[it];
+          if (row < M) {
+            unsigned short *dst = y + (int64_t)row * ld_y + col;
+            if (vec_ok && col + 8 <= N) {
+              *(v4u *)dst = v;
+            } else {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sav[i][r] = sa[min(m0 + wm * WM + i * 32 + 8 * (r >> 2) + lrow + (r & 3), M - 1)];
-    }
-    uint8_t *ot = smem + (KT % STAGES) * STAGE_BYTES + wave * HROWS * PITCH;
-    const bool vec_ok = ((uintptr_t)y % 16 == 0) && (ld_y % 8 == 0);
-    constexpr int PIECES = WN / 8;   // 16-byte pieces per row
-    constexpr int PASSES = HROWS * PIECES / 64;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int trow = 8 * (r >> 2) + lrow + (r & 3);   // row within the 32 staged rows
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          float val;
-          if constexpr (GROUPED)
-            val = facc[i][j][r];
-          else
-            val = (float)acc[i][j][r] * (sav[i][r] * swv[j]);
-          *(unsigned short *)(ot + trow * PITCH + (j * 32 + lcol) * 2) = float_to_half_bits(val);
-        }
-      }
-      // the wave reads back only what it wrote itself: LDS operations of one
-      // wave complete in order, no barrier needed
-      v4u pv[PASSES];   // all reads first, then the (edge-guarded) stores
-#pragma unroll
-      for (int it = 0; it < PASSES; ++it) {
-        const int p = it * 64 + lane;
-        pv[it] = *(const v4u *)(ot + (p / PIECES) * PITCH + (p % PIECES) * 16);
-      }
-#pragma unroll
-      for (int it = 0; it < PASSES; ++it) {
-        const int p = it * 64 + lane;
-        const int trow = p / PIECES, cp = p % PIECES;
-        const int row = m0 + wm * WM + i * HROWS + trow;
-        const int col = n0 + wn * WN + cp * 8;
-        const v4u v = pv[it];
-        if (row < M) {
-          unsigned short *dst = y + (int64_t)row * ld_y + col;
-          if (vec_ok && col + 8 <= N) {
-            *(v4u *)dst = v;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (col + e < N) dst[e] = (unsigned short)(v[e >> 1] >> (16 * (e & 1)));
+              for (int e = 0; e < 8; ++e)
+                if (col + e < N) dst[e] = (unsigned short)(v[e >> 1] >> (16 * (e & 1)));
+            }
           }
         }
       }
+      // K-tile 1 of the next tile: once every wave has read its staged rows
+      // back (its loads then follow this tile's stores, which the next
+      // tile's first wait does not need to cover)
+      if (has_next && KT > 1) {
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        issue(1, 1);
+      }
     }
+    if (!has_next) break;
+    bid = nbid;
+    m0 = dm0;
+    n0 = dn0;
   }
 }
 
@@ -599,7 +680,11 @@ hipError_t launch_cfg(const uint8_t *a, const float *sa, const uint8_t *w, const
                       int64_t N, int64_t K, int group, void *y, int64_t ld_y, bool out_i32,
                       hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
+  // persistent shapes: as many blocks as are resident at once (a multiple
+  // of 8, the XCD count); otherwise one per tile
+  const int64_t resident = (int64_t)device_cu_count() * (OCC * 4 / (WAVES_M * WAVES_N)) / 8 * 8;
+  const int64_t nblocks = persistent_shape(BM, GROUPED) && resident >= 8 && tiles > resident ? resident : tiles;
+  dim3 grid((unsigned)nblocks), block(64 * WAVES_M * WAVES_N);
 #define QR_GEMM_LAUNCH(I32, TAIL)                                                                \
   gemm_prefill_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, GROUPED, I32, TAIL, OCC, CB><<<grid, block, 0, stream>>>( \
       a, sa, w, sw, (int)M, (int)N, (int)K, group, y, ld_y)
