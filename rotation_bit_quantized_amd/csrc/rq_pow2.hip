@@ -170,14 +170,9 @@ __global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
   }
   if (wave_id >= rows) return;
 
-  // DMA of row r into buffer b.  Rows past the end re-read the wave's own
-  // first row (their buffers are never read), which keeps the number of
-  // vector memory instructions per row uniform and the vmcnt waits below
-  // exact; each wave re-reads a different row, so the redundant reads do not
-  // all converge on one address (with one row per wave, every wave's
-  // follower DMA used to hit the matrix's last row at once).
+  // DMA of row r (< rows) into buffer b.
   auto issue_row = [&](int64_t r, int b) {
-    const uint8_t *src = (const uint8_t *)(x + (r < rows ? r : wave_id) * ld_x);
+    const uint8_t *src = (const uint8_t *)(x + r * ld_x);
 #pragma unroll
     for (int i = 0; i < DMA; ++i)
       __builtin_amdgcn_global_load_lds((const void *)(src + 1024 * i + 16 * lane),
@@ -200,7 +195,9 @@ __global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
   }
 
   issue_row(wave_id, 0);
-  if constexpr (kBufs == 2) issue_row(wave_id + wave_stride, 1);
+  if constexpr (kBufs == 2) {
+    if (wave_id + wave_stride < rows) issue_row(wave_id + wave_stride, 1);
+  }
 
   if constexpr (!SIGNS_LDS) {
 #pragma unroll
@@ -218,14 +215,23 @@ __global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
   for (int64_t row = wave_id; row < rows; row += wave_stride, ++it) {
     const uint8_t *buf = bufs + (kBufs == 2 ? (it & 1) * ROWB : 0);
     // Wait for this row's DMA.  Two buffers: issued after it are the DMA of
-    // the following row (always), the stores of the previous row (it >= 1)
-    // and of the one before, with the DMA of this row's follower in between
-    // (it >= 2).  One buffer: only the previous row's stores (it >= 1).
-    // The sign words, where loaded, went out before the first row's DMA.
+    // the wave's following row (when that row exists; DMAs of rows past the
+    // end are not issued), the stores of the previous row (it >= 1) and of
+    // the one before (it >= 2).  One buffer: only the previous row's stores
+    // (it >= 1).  The sign words, where loaded, went out before the first
+    // row's DMA.  The branches are wave-uniform.
     if constexpr (kBufs == 2) {
-      if (it == 0) wait_vm<DMA>();
-      else if (it == 1) wait_vm<DMA + STORES>();
-      else wait_vm<DMA + 2 * STORES>();
+      const bool follower = row + wave_stride < rows;
+      if (it == 0) {
+        if (follower) wait_vm<DMA>();
+        else wait_vm<0>();
+      } else if (it == 1) {
+        if (follower) wait_vm<DMA + STORES>();
+        else wait_vm<STORES>();
+      } else {
+        if (follower) wait_vm<DMA + 2 * STORES>();
+        else wait_vm<2 * STORES>();
+      }
     } else {
       if (it > 0) wait_vm<STORES>();
       else wait_vm<0>();
@@ -253,10 +259,14 @@ __global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
         }
       }
     }
-    // every read has returned: the buffer takes its next row
+    // every read has returned: the buffer takes its next row (none past the
+    // end: the waits above count only the DMAs of rows that exist)
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    if constexpr (kBufs == 2) issue_row(row + 2 * wave_stride, it & 1);
-    else issue_row(row + wave_stride, 0);
+    if constexpr (kBufs == 2) {
+      if (row + 2 * wave_stride < rows) issue_row(row + 2 * wave_stride, it & 1);
+    } else if (row + wave_stride < rows) {
+      issue_row(row + wave_stride, 0);
+    }
 
     float v[NV];
 #pragma unroll
