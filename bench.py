@@ -106,6 +106,7 @@ KERNEL_SOURCES = {
     "gemm_decode_lds_kernel": [CSRC + "gemm_decode.hip", CSRC + "qr_common.h"],
     "rq_kron_kernel": [CSRC + "rq_kron.hip", CSRC + "qr_common.h"],
     "rq_pow2_kernel": [CSRC + "rq_pow2.hip", CSRC + "qr_common.h"],
+    "kv_quant_kernel": [CSRC + "kv_quant.hip", CSRC + "qr_common.h"],
 }
 
 
@@ -216,8 +217,9 @@ def cpu_baseline(cfg, rows, kv_rows):
 # ---------------------------------------------------------------- counters
 
 def ingest_pmc(cfg_name, fetch_dir, write_dir, calib_mib):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the step's GEMM and of its
-    rotate-quant kernel, and of the calibration copy; scale each kernel's by
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the step's GEMM, of its
+    rotate-quant kernel and (c2, c5) of its KV quantizer, and of the
+    calibration copy; scale each kernel's by
     known/measured of the copy (a copy of B bytes reads B and writes B).  The
     median over a kernel's dispatches is taken, so the one weight-preparation
     launch of the rotate-quant kernel (another row count) does not count."""
@@ -262,7 +264,10 @@ def ingest_pmc(cfg_name, fetch_dir, write_dir, calib_mib):
         recs = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         recs = {}
-    for key, kernel in ((f"int4_gemm_{cfg_name}", gemm), (f"rotate_quant_{cfg_name}", rq)):
+    kinds = [(f"int4_gemm_{cfg_name}", gemm), (f"rotate_quant_{cfg_name}", rq)]
+    if any("kv_quant_kernel" in k for (d, k) in fetch):
+        kinds.append((f"kv_quant_{cfg_name}", "kv_quant_kernel"))
+    for key, kernel in kinds:
         k_fetch, n, kname = kernel_median(fetch, kernel)
         k_write, _, _ = kernel_median(write, kernel)
         m = re.search(kernel + r"<[^>]*>", kname)
