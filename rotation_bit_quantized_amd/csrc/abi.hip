@@ -1,6 +1,7 @@
 // The exported C ABI (include/qr.h): argument validation on the host, then
-// dispatch to the kernels.  Nothing here allocates, synchronises or keeps
-// state; a rejected call launches nothing.
+// dispatch to the kernels.  Nothing here allocates or synchronises; the only
+// state kept is, per device, the address of the static scratch array below
+// (and the CU count, in the launchers); a rejected call launches nothing.
 #include "../../include/qr.h"
 #include "qr_launch.h"
 
