@@ -14,7 +14,9 @@ compared with the oracle on sampled outputs.
   (64 tiles per wave), with and without signs;
 * integer GEMM: exact int32 sums on sampled outputs at 2048 x 12288 x 4096 and
   131072 x 4096 x 11008 (the fp16 outputs at full size are checked in
-  test_gpu_parity.py).
+  test_gpu_parity.py), and a ragged shape with more tiles than resident
+  blocks (4000 x 9000 x 1152: ~3 tiles per persistent block, partial tiles
+  on both edges, a half K-tile at the end), int32 and fp16.
 
 Samples always hold the first rows (first iteration of every wave), bands in
 the middle and the last rows (last iterations), and random rows in between,
@@ -28,7 +30,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from tests.parity import check_kv, check_scales, check_symmetric_codes, check_symmetric_int8
+from tests.parity import (check_kv, check_output, check_scales, check_symmetric_codes, check_symmetric_int8,
+                          epilogue_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -165,3 +168,26 @@ def test_gemm_i32_full_size_sampled_exact(qr, cfg):
     got = host(acc[torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(cols, device="cuda")])
     ref = O.int_gemm(O.unpack_int4(a[rows]), O.unpack_int4(w[cols]))
     assert np.array_equal(got.astype(np.int64), ref)
+
+
+def test_gemm_persistent_ragged_sampled(qr):
+    """4000 x 9000 x 1152: the 256 x 192 tiles (16 x 47 of them, partial on
+    both edges) run on the persistent grid, about three per block, K ends in
+    a half tile.  Exact int32 sums and the fp16 output (per-element epilogue
+    bound) on sampled rows, all columns."""
+    M, N, K = 4000, 9000, 1152
+    a = W.make_random_packed(M, K // 2, seed=31)
+    w = W.make_random_packed(N, K // 2, seed=32)
+    rng = np.random.default_rng(33)
+    sa = (rng.random(M) * 0.1 + 0.01).astype(np.float32)
+    sw = (rng.random(N) * 0.01 + 0.001).astype(np.float32)
+    acc = qr.int4_gemm_i32(dev(a), dev(w))
+    y = qr.int4_gemm(dev(a), dev(sa), dev(w), dev(sw))
+    rows = sample(M, seed=7, head=40, band=40, tail=40, rand=40)
+    ridx = torch.as_tensor(rows, device="cuda")
+    ref = O.int_gemm(O.unpack_int4(a[rows]), O.unpack_int4(w))
+    assert np.array_equal(host(acc[ridx]).astype(np.int64), ref)
+    yref = O.dequantize_output(ref, sa[rows], sw)
+    yg = host(y[ridx])
+    check_output(yg, yref)
+    assert np.all(np.abs(yg.astype(np.float64) - yref) <= epilogue_bound(ref, sa[rows], sw))
