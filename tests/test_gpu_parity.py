@@ -459,3 +459,40 @@ def test_kv_strided_slice_of_qkv(qr):
         codes, step, zero = qr.kv_quant(view)
         ref = np.ascontiguousarray(qkv[:, part * H * 128:(part + 1) * H * 128]).reshape(T, H, 128)
         check_kv(host(codes), host(step), host(zero), ref)
+
+
+# ------------------------------------------------------------------ empty inputs
+
+def test_empty_inputs_every_entry_point(qr):
+    """Zero rows, tokens, channels or sequences: every call returns empty (or
+    untouched) outputs and launches nothing that could fail."""
+    cuda = "cuda"
+    u8, f32, f16 = torch.uint8, torch.float32, torch.float16
+    # rotate-quant: power of two, Kronecker, 6/8 bits, fused SwiGLU
+    c, s = qr.rotate_quant(torch.zeros((0, 11008), dtype=f16, device=cuda),
+                           qr.Rotation.kronecker(64, W.make_dense(W.CONFIGS["c3"])))
+    assert c.shape == (0, 5504) and s.shape == (0,)
+    c, s = qr.rotate_quant_i8(torch.zeros((0, 4096), dtype=f16, device=cuda), qr.Rotation.hadamard(4096), 8)
+    assert c.shape == (0, 4096)
+    c, s = qr.swiglu_rotate_quant(torch.zeros((0, 1024), dtype=f16, device=cuda),
+                                  torch.zeros((0, 1024), dtype=f16, device=cuda), qr.Rotation.hadamard(1024))
+    assert c.shape == (0, 512)
+    # GEMM with M = 0 or N = 0, prefill and decode sizes
+    for M, N in ((0, 256), (64, 0), (0, 0)):
+        y = qr.int4_gemm(torch.zeros((M, 2048), dtype=u8, device=cuda), torch.zeros(M, dtype=f32, device=cuda),
+                         torch.zeros((N, 2048), dtype=u8, device=cuda), torch.zeros(N, dtype=f32, device=cuda))
+        assert y.shape == (M, N)
+        acc = qr.int4_gemm_i32(torch.zeros((M, 2048), dtype=u8, device=cuda),
+                               torch.zeros((N, 2048), dtype=u8, device=cuda))
+        assert acc.shape == (M, N)
+    # KV quant of no tokens
+    codes, scales, zeros = qr.kv_quant(torch.zeros((0, 32, 128), dtype=f16, device=cuda))
+    assert codes.shape == (0, 32, 64) and scales.shape == (0, 32) and zeros.shape == (0, 32)
+    # decode attention over empty sequences: zeros
+    B, Hq, Hkv, T = 2, 8, 8, 16
+    q = torch.randn((B, Hq, 128), dtype=f16, device=cuda)
+    kc = torch.zeros((B, T, Hkv, 64), dtype=u8, device=cuda)
+    ks = torch.ones((B, T, Hkv), dtype=f32, device=cuda)
+    kz = torch.zeros((B, T, Hkv), dtype=u8, device=cuda)
+    out = qr.kv_attn_decode(q, kc, ks, kz, kc, ks, kz, lens=[0, 0])
+    assert torch.count_nonzero(out).item() == 0
