@@ -22,7 +22,7 @@ before timing; weights are prepared on the GPU before timing (rotate +
 quantize the rows of W^T with the same library call).  Steps cycle over enough
 distinct buffer sets (>= 1 GiB, at least two) that nothing is served from the
 256 MB Infinity Cache between uses, and consecutive steps alternate over
---streams HIP streams of default priority (a buffer set is reused only after
+HIP streams of default priority (--streams; a buffer set is reused only after
 the step that last used it has finished: an event dependency).
 
 Prints one JSON line.  `value` is whole-step throughput in TOPS (2 M N K per
@@ -33,7 +33,7 @@ bounded row sample of the same workload and extrapolated to the whole step;
 `peaks_measured` holds what this GPU attains for a streaming copy and for
 back-to-back int8 / fp16 MFMAs (include/qr_peaks.h), the second denominators.
 
-  python bench.py [--config c3] [--steps 20] [--warmup 5] [--streams 2] [--no-cpu]
+  python bench.py [--config c3] [--steps 20] [--warmup 5] [--streams N] [--no-cpu]
   python bench.py --suite [--only case,...]      # every kernel at every shape
 """
 from __future__ import annotations
@@ -58,6 +58,11 @@ FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA, published (2.5 PFLOP/s)
 CACHE_BYTES = 1 << 30        # cycle buffers over >= 1 GiB (MALL is 256 MB)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 STEP_CONFIGS = ("c3", "c2", "c4", "c5")
+# Steps alternate over this many HIP streams unless --streams says otherwise:
+# overlapping consecutive steps helps the short latency-bound launches of c2
+# and c5, and costs ~2% at c3 (5.64 vs 5.75-5.78 ms per step in one process),
+# where each kernel fills the GPU by itself.
+DEFAULT_STREAMS = {"c3": 1, "c4": 1, "c2": 2, "c5": 2}
 # token rows of the CPU oracle sample per config (about 5-20 s on 16 cores)
 CPU_ROWS = {"c2": 2048, "c3": 2048, "c4": 512, "c5": 64}
 METRIC = "rotate+quant+int4 GEMM TOPS and GB/s at 7B/70B layer shapes; % of roofline"
@@ -71,8 +76,10 @@ def parse():
     ap.add_argument("--config", default="c3", choices=STEP_CONFIGS)
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows in the CPU oracle sample (0 = default)")
-    ap.add_argument("--streams", type=int, default=2,
-                    help="HIP streams the steps alternate over (1: strictly one step after another)")
+    ap.add_argument("--streams", type=int, default=0,
+                    help="HIP streams the steps alternate over (1: strictly one step after another; 0: the "
+                         "workload's default, 2 for the short c2 and c5 steps whose latency-bound launches "
+                         "gain from overlapping, 1 for c3 and c4 whose kernels each fill the GPU)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run one probe copy of this many MiB (HBM counter calibration)")
@@ -368,7 +375,8 @@ def run_step(args):
                 s["kv"] = kv0 if i == 0 else kv0.clone()
         sets.append(s)
     del x0, wc0, ws0
-    streams = [stream] + [torch.cuda.Stream(device=dev) for _ in range(max(1, args.streams) - 1)]
+    nstreams = args.streams if args.streams > 0 else DEFAULT_STREAMS[cfg.name]
+    streams = [stream] + [torch.cuda.Stream(device=dev) for _ in range(max(1, nstreams) - 1)]
 
     def rq(s, st=stream):
         qr.rotate_quant(s["x"], rot, group, codes=s["xc"], scales=s["xs"], stream=st)
