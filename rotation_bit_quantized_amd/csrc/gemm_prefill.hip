@@ -40,6 +40,11 @@
 // v_mfma_i32_32x32x32_i8, so each widened operand feeds FN (or FM) MFMAs.
 // The host picks the block shape whose tile count fills the CU slots best.
 //
+// Tiles: the 256 x 192 shape with per-channel scales runs persistent blocks
+// (one per CU, each looping over every gridDim-th tile); the next tile's
+// output scales and first two K-tiles are fetched while the current tile's
+// epilogue runs.  The other shapes run one block per tile.
+//
 // 8-bit codes (the 6- and 8-bit RTN variants; QuaRot abstract: lossless 6-
 // and 8-bit RTN): the same kernel with CB = 8.  A K-tile is still 128 bytes
 // per row, now 128 codes; a 16-byte fragment read is one MFMA k-step used as
