@@ -43,7 +43,8 @@
 //    waves through LDS.  Codes are packed eight to a word in registers, a
 //    4 x 4 nibble transpose within lane quads (DPP, v_perm, v_alignbit) makes
 //    each 16-bit half four consecutive codes of one output row, and the
-//    block stores the row from LDS as 16-byte chunks.
+//    block stores the row from LDS as 16-byte chunks after the next row's
+//    first barrier (two barriers per row).
 #include "qr_common.h"
 #include "qr_launch.h"
 
@@ -156,15 +157,33 @@ __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron_kernel(
   uint8_t *crow = codes + row0 * (int64_t)code_bytes;
   float *srow = scales + row0;
   const int64_t c_step = (int64_t)stride * code_bytes;
+  // The codes of row r_{k-1}, staged in LDS at the end of step k - 1, are
+  // stored after step k's first barrier (which every wave passes after
+  // staging them): one barrier per row fewer.  Step k's own codes are staged
+  // only after its absmax barrier, which every wave passes after reading
+  // r_{k-1}'s from LDS.
+  auto store_codes = [&](uint8_t *cr, float *sr, float smax) __attribute__((always_inline)) {
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const int ch = cs_chunk(pp);
+      const int grp = ch / half_m, within = ch - grp * half_m;
+      const v4u v = *(const v4u *)(aux + grp * kGroupPitch + 16 * within);
+      *(v4u *)(cr + 16 * ch) = v;
+    }
+    if (tid == 0) *sr = smax * scale_mul;
+  };
+  float prev_mx = 0.f;
   int xb = 0, db = 2;
   for (int k = 0; k < nblk; ++k) {
-    // Row r_k has landed.  Issued after its DMA: for k = 0 the DMA of r_1
-    // (kKS operations); for k >= 1 at least the DMA of r_{k+1} and the two
-    // code stores of r_{k-1} per wave (the scale store of wave 0 only adds).
-    if (k == 0) wait_vm<kKS>();
+    // Row r_k has landed.  Issued after its DMA (in step k - 2): the DMA of
+    // r_{k+1} (kKS operations, in step k - 1) and, for k >= 2, the two code
+    // stores of r_{k-2} per wave before it (the scale store of wave 0 only
+    // adds).
+    if (k < 2) wait_vm<kKS>();
     else wait_vm<kKS + 2>();
     wait_lgkm0();
-    __builtin_amdgcn_s_barrier();   // every wave's part of r_k is in; r_{k-1}'s buffer is free
+    __builtin_amdgcn_s_barrier();   // every wave's part of r_k is in; r_{k-1}'s buffer and codes are ready
+    if (k > 0) store_codes(crow - c_step, srow - stride, prev_mx);
     const uint8_t *xbuf = smem + xb * kRowBuf;
     const uint8_t *nsrc = row_src(k + 2);
 
@@ -285,23 +304,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron_kernel(
         for (int h = 0; h < 2; ++h)
           *(unsigned short *)(aux + cw + (2 * R + h) * kGroupPitch) = (unsigned short)(v >> (16 * h));
       }
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();   // the row's codes are staged (and every wave has read the maxima)
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const int ch = cs_chunk(pp);
-      const int grp = ch / half_m, within = ch - grp * half_m;
-      const v4u v = *(const v4u *)(aux + grp * kGroupPitch + 16 * within);
-      *(v4u *)(crow + 16 * ch) = v;
-    }
-    if (tid == 0) *srow = mx * scale_mul;
-    // the next row's maxima and codes may only be written once every wave
-    // has read these: the barrier at the top of the next row orders that
+    // every wave has read the maxima before the next row's first barrier,
+    // and writes the next maxima only after it
+    prev_mx = mx;
     crow += c_step;
     srow += stride;
     xb = xb == kRowBufs - 1 ? 0 : xb + 1;
     db = db == kRowBufs - 1 ? 0 : db + 1;
   }
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();   // the last row's codes are staged
+  store_codes(crow - c_step, srow - stride, prev_mx);
   wait_vm<0>();   // no DMA may still be writing this block's LDS when it exits
 }
 
