@@ -95,6 +95,9 @@ def parse():
                     help="digest a rocprofv3 kernel trace of this script (per kernel, all dispatches and the "
                          "last --trace-last ones) and exit")
     ap.add_argument("--trace-last", type=int, default=20, help="dispatches of the per-launch timing phase")
+    ap.add_argument("--codes-sweep", action="store_true",
+                    help="the config's int4 GEMM looped ~2 s each on constant, workload and uniformly random "
+                         "codes, with the shader clock sampled by rocm-smi meanwhile (one JSON line per kind)")
     return ap.parse_args()
 
 
@@ -171,6 +174,25 @@ def measure_peaks(dev):
                   "chains, "
                   "20000 rounds; medians of 5")
     return out
+
+
+def measure_codes_peak(a_codes, w_codes, stream, seconds=0.5):
+    """The int8 MFMA loop of qr_peak_mfma_codes on the step's own activation
+    and weight codes, run for about `seconds` so that the clock has settled
+    to what this operand data draws (it drops within ~0.1-0.4 s of dense
+    MFMA work); median of the second half of the calls."""
+    import rotation_bit_quantized_amd as qr
+    a = a_codes.reshape(-1)
+    w = w_codes.reshape(-1)
+    a = a[: a.numel() // 16 * 16]
+    w = w[: w.numel() // 16 * 16]
+    iters = 20000                                   # ~20 ms per call
+    buf, ops = qr.peak_mfma_codes(a, w, iters)
+    times, t0 = [], time.perf_counter()
+    while time.perf_counter() - t0 < seconds or len(times) < 10:
+        ms, _ = time_each(lambda i: qr.peak_mfma_codes(a, w, iters, buf), 1, stream, warm=0)
+        times.append(ms)
+    return round(ops / (statistics.median(times[len(times) // 2:]) * 1e-3) / 1e12, 1)
 
 
 # ---------------------------------------------------------------- the oracle on a row sample
@@ -451,6 +473,13 @@ def run_step(args):
     gemm_ms, gemm_mean = time_each(lambda i: gemm(sets[i % nsets]), nrep, stream)
     kv_ms = time_each(lambda i: kv(sets[i % nsets]), nrep, stream) if has_kv else None
 
+    # the int8 MFMA rate attainable on this step's own codes (prefill)
+    if peaks and M > 64:
+        peaks["mfma_int8_codes_TOPS"] = measure_codes_peak(sets[0]["xc"], sets[0]["wc"], stream)
+        peaks["how_codes"] = ("qr_peak_mfma_codes: the kind-0 loop on operands widened from the step's activation "
+                              "codes (A) and weight codes (W), run ~0.5 s so that the clock settles; median of "
+                              "the second half of ~20 ms calls")
+
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
     rq_bytes = M * K * 2 + M * K // 2 + M * G * 4
@@ -474,6 +503,8 @@ def run_step(args):
         "int4_gemm": {"kernel": "gemm_decode_lds_kernel" if M <= 64 else "gemm_prefill_kernel",
                       "us_median": round(gemm_ms * 1e3, 3), "us_mean": round(gemm_mean * 1e3, 3),
                       "TOPS": round(gemm_tops, 2), **frac(gemm_tops, INT8_PEAK_TOPS, "mfma_int8_TOPS"),
+                      **({"frac_measured_codes_peak": round(gemm_tops / peaks["mfma_int8_codes_TOPS"], 4)}
+                         if peaks and "mfma_int8_codes_TOPS" in peaks else {}),
                       "GB/s": round(gemm_gbs, 1), "frac_hbm": round(gemm_gbs / HBM_PEAK_GBS, 4),
                       "bytes": gemm_bytes},
     }
@@ -539,6 +570,83 @@ def run_step(args):
             kv_rows = lambda y: [k_host[:rows], v_host[:rows]]
         out["cpu_baseline"] = cpu_baseline(cfg, rows, kv_rows)
     print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------- clock vs operand data
+
+def sclk_mhz():
+    """Current shader clock from rocm-smi (None if it cannot be read)."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"sclk clock level:[^(]*\((\d+)Mhz\)", txt)
+    return int(m.group(1)) if m else None
+
+
+def codes_sweep(args):
+    """The same GEMM launch on three kinds of operand data.  The instruction
+    stream is identical; only the bits the MFMAs toggle differ, and with them
+    the clock this part sustains under the kernel."""
+    import threading
+    import torch
+    import workloads as W
+    import rotation_bit_quantized_amd as qr
+    qr.library()
+    cfg = W.CONFIGS[args.config]
+    M, N, K, group = cfg.M, cfg.N, cfg.K, cfg.group
+    if M <= 64:
+        raise SystemExit("--codes-sweep is for the prefill configs")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    signs, dense = W.make_signs(cfg), W.make_dense(cfg)
+    rot = (qr.Rotation.kronecker(cfg.had_n, dense, signs) if cfg.dense_m > 1 else qr.Rotation.hadamard(K, signs))
+    wt = torch.from_numpy(np.ascontiguousarray(W.make_w(cfg).T)).to(dev)
+    wc, ws = qr.rotate_quant(wt, rot, group)
+    del wt
+    x = torch.from_numpy(W.make_x(cfg)).to(dev)
+    xc, xs = qr.rotate_quant(x, rot, group)
+    del x
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    kinds = [("constant", torch.full_like(xc, 0x35), torch.full_like(wc, 0x17)),
+             ("workload", xc, wc),
+             ("uniform", torch.randint(0, 256, xc.shape, dtype=torch.uint8, device=dev, generator=g),
+              torch.randint(0, 256, wc.shape, dtype=torch.uint8, device=dev, generator=g))]
+    for name, a, w in kinds:
+        qr.int4_gemm(a, xs, w, ws, group, y=y)
+        torch.cuda.synchronize()
+        clocks, stop = [], threading.Event()
+
+        def sample():
+            while not stop.wait(0.25):
+                c = sclk_mhz()
+                if c is not None:
+                    clocks.append(c)
+        th = threading.Thread(target=sample)
+        th.start()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0, n = time.perf_counter(), 0
+        e0.record()
+        while time.perf_counter() - t0 < 2.0:
+            for _ in range(10):
+                qr.int4_gemm(a, xs, w, ws, group, y=y)
+            torch.cuda.synchronize()
+            n += 10
+        e1.record()
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        late = clocks[len(clocks) // 3:]
+        print(json.dumps({"codes": name, "config": cfg.name, "launches": n, "us_per_launch": round(us, 1),
+                          "TOPS": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1),
+                          "sclk_MHz_median": statistics.median(late) if late else None,
+                          "sclk_samples": len(clocks)}), flush=True)
+        time.sleep(1.0)
 
 
 # ---------------------------------------------------------------- per-kernel suite
@@ -692,7 +800,13 @@ def suite(args):
              bytes=nbytes, workspace=wsb, cache_sets=nsets)
 
     if not only or "peaks" in only:
-        emit("peaks", **measure_peaks(dev))
+        pk = measure_peaks(dev)
+        # the suite's GEMM cases multiply uniformly random codes: the same
+        # MFMA loop on such codes is their data-matched ceiling
+        ra, rw = codes(4096, 32768), codes(4096, 32768)
+        pk["mfma_int8_random_codes_TOPS"] = measure_codes_peak(ra, rw, st)
+        del ra, rw
+        emit("peaks", **pk)
     rq_case("rq_c2", "c2", 2048, 0)
     rq_case("rq_c4_g128", "c4", 16384, 128)
     rq_case("rq_c5", "c5", 64, 0)
@@ -729,6 +843,9 @@ def main():
               f"(the hot path is per-token independent and would shard tokens across GPUs with no exchange).",
               file=sys.stderr)
         sys.exit(2)
+    if args.codes_sweep:
+        codes_sweep(args)
+        return
     if args.suite:
         import torch
         import rotation_bit_quantized_amd as qr

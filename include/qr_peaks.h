@@ -42,6 +42,23 @@ int64_t qr_peak_mfma_waves(void);
  */
 qr_status qr_peak_mfma(int64_t kind, int64_t iters, int32_t *out, void *stream);
 
+/*
+ * The int8 MFMA loop of kind 0 on operands taken from packed int4 codes (two
+ * per byte, as qr_rotate_quant writes them), widened once to the int8 form
+ * the int4 GEMM multiplies (16 q): wave v, lane l loads the 16-byte pieces
+ * ((64 v + l) * 8 + f) mod (bytes / 16), f < 8, of `a` (A operands) and of
+ * `w` (W operands), then issues `iters` (1 .. 2^24) rounds of 32
+ * v_mfma_i32_32x32x32_i8 over four accumulators.  On dense MFMA work this
+ * part lowers its clock as more operand bits toggle, so with a workload's
+ * own codes this is the int8 rate attainable on that data.  a_bytes and
+ * w_bytes: multiples of 16, at least 16 (else QR_ESHAPE); a, w 16-byte
+ * aligned, out 4-byte aligned (QR_EALIGN); null pointers QR_EINVAL.  Work per
+ * call = waves * iters * 32 * 65536 int8 ops (waves = qr_peak_mfma_waves()).
+ * `out` receives, per lane, the int32 sum of its 64 accumulator values.
+ */
+qr_status qr_peak_mfma_codes(const uint8_t *a, int64_t a_bytes, const uint8_t *w, int64_t w_bytes, int64_t iters,
+                             int32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

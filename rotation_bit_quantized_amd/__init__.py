@@ -23,7 +23,7 @@ __all__ = [
     "QRError", "LibraryNotBuilt", "Rotation", "library", "library_path", "rotate_quant", "int4_gemm",
     "int4_gemm_i32", "kv_quant", "kv_attn_decode", "kv_attn_decode_workspace", "rotate_quant_i8",
     "int8_gemm", "int8_gemm_i32", "swiglu_rotate_quant", "status_str", "version", "EXPORTS",
-    "peak_copy", "peak_mfma",
+    "peak_copy", "peak_mfma", "peak_mfma_codes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +35,7 @@ EXPORTS = ("qr_rotate_quant", "qr_int4_gemm", "qr_kv_quant", "qr_int4_gemm_i32",
            "qr_kv_attn_decode_workspace", "qr_kv_attn_decode_noalloc", "qr_rotate_quant_i8", "qr_int8_gemm",
            "qr_int8_gemm_i32", "qr_swiglu_rotate_quant", "qr_status_str", "qr_version",
            # measurement probes (include/qr_peaks.h)
-           "qr_peak_copy", "qr_peak_mfma", "qr_peak_mfma_waves")
+           "qr_peak_copy", "qr_peak_mfma", "qr_peak_mfma_waves", "qr_peak_mfma_codes")
 
 
 class QRError(RuntimeError):
@@ -96,6 +96,8 @@ def library():
     lib.qr_peak_mfma.restype = st
     lib.qr_peak_mfma_waves.argtypes = []
     lib.qr_peak_mfma_waves.restype = i64
+    lib.qr_peak_mfma_codes.argtypes = [vp, i64, vp, i64, i64, vp, vp]
+    lib.qr_peak_mfma_codes.restype = st
     lib.qr_status_str.argtypes = [st]
     lib.qr_status_str.restype = ctypes.c_char_p
     lib.qr_version.argtypes = []
@@ -504,3 +506,20 @@ def peak_mfma(kind: int, iters: int, out=None, stream=None):
     _check("qr_peak_mfma", library().qr_peak_mfma(int(kind), int(iters), _ptr(out), _stream(stream)))
     per = {0: 65536, 1: 16384, 2: 32768, 3: 32768}[int(kind)]
     return out, waves * int(iters) * 4 * per
+
+
+def peak_mfma_codes(a_codes: torch.Tensor, w_codes: torch.Tensor, iters: int, out=None, stream=None):
+    """qr_peak_mfma_codes: the int8 32x32x32 MFMA loop on operands widened from
+    the packed int4 codes a_codes (A side) and w_codes (W side), contiguous
+    uint8 GPU tensors of a multiple of 16 bytes.  Returns (out, ops per call)."""
+    waves = int(library().qr_peak_mfma_waves())
+    for name, t in (("a_codes", a_codes), ("w_codes", w_codes)):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 tensor")
+    if out is None:
+        out = torch.empty((waves * 64,), dtype=torch.int32, device="cuda")
+    _need(out, torch.int32, "out", (waves * 64,), True)
+    _on_gpu(a_codes=a_codes, w_codes=w_codes, out=out)
+    _check("qr_peak_mfma_codes", library().qr_peak_mfma_codes(
+        _ptr(a_codes), a_codes.numel(), _ptr(w_codes), w_codes.numel(), int(iters), _ptr(out), _stream(stream)))
+    return out, waves * int(iters) * 32 * 65536

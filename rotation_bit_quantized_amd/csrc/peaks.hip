@@ -105,6 +105,46 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, int *__restri
   }
 }
 
+// Back-to-back v_mfma_i32_32x32x32_i8 on operands taken from the caller's
+// packed int4 codes, widened once to the GEMM's high-nibble int8 form
+// (16 q): each lane loads eight 16-byte A pieces and eight W pieces (piece
+// (64 wave + lane) * 8 + f, wrapping over each buffer), then every round
+// issues 32 MFMAs over four accumulator chains in the GEMM's order
+// (consecutive MFMAs share the A operand and change the W one).  The chip's
+// clock under dense MFMA work depends on how many operand bits toggle, so on
+// the codes of a real workload this loop gives the rate the matrix cores
+// attain for that data, below the constant-operand loop above.
+__global__ __launch_bounds__(256) void peak_mfma_codes_kernel(const v4u *__restrict__ a, int64_t a_pieces,
+                                                               const v4u *__restrict__ w, int64_t w_pieces,
+                                                               int iters, int *__restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  v4i opa[8][2], opw[8][2];
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    const int64_t piece = (wave * 64 + lane) * 8 + f;
+    widen_hi_nibble(a[piece % a_pieces], opa[f][0], opa[f][1]);
+    widen_hi_nibble(w[piece % w_pieces], opw[f][0], opw[f][1]);
+  }
+  v16i c[4] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          c[2 * ks + j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(opa[f][ks], opw[(f + 4 * j) & 7][ks], c[2 * ks + j],
+                                                                0, 0, 0);
+  }
+  int s = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c[q][r];
+  out[wave * 64 + lane] = s;
+}
+
 }  // namespace
 }  // namespace qr
 
@@ -141,6 +181,18 @@ qr_status qr_peak_mfma(int64_t kind, int64_t iters, int32_t *out, void *stream) 
     qr::peak_mfma_kernel<2><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((int)iters, out);
   else
     qr::peak_mfma_kernel<3><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((int)iters, out);
+  return hipGetLastError() == hipSuccess ? QR_OK : QR_EDEVICE;
+}
+
+qr_status qr_peak_mfma_codes(const uint8_t *a, int64_t a_bytes, const uint8_t *w, int64_t w_bytes, int64_t iters,
+                             int32_t *out, void *stream) {
+  if (a == nullptr || w == nullptr || out == nullptr) return QR_EINVAL;
+  if (a_bytes < 16 || w_bytes < 16 || a_bytes % 16 != 0 || w_bytes % 16 != 0) return QR_ESHAPE;
+  if (iters <= 0 || iters > ((int64_t)1 << 24)) return QR_ESHAPE;
+  if (((uintptr_t)a & 15) || ((uintptr_t)w & 15) || ((uintptr_t)out & 3)) return QR_EALIGN;
+  const int64_t blocks = (int64_t)qr::device_cu_count() * 2;   // 8 waves per CU, two per SIMD
+  qr::peak_mfma_codes_kernel<<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>(
+      (const qr::v4u *)a, a_bytes / 16, (const qr::v4u *)w, w_bytes / 16, (int)iters, out);
   return hipGetLastError() == hipSuccess ? QR_OK : QR_EDEVICE;
 }
 

@@ -39,6 +39,13 @@ def test_peak_probes_reject_bad_arguments():
     assert lib.qr_peak_mfma(-1, 10, A16, None) == qr.QR_EINVAL
     assert lib.qr_peak_mfma(0, 0, A16, None) == qr.QR_ESHAPE
     assert lib.qr_peak_mfma(0, 10, None, None) == qr.QR_EINVAL
+    assert lib.qr_peak_mfma_codes(None, 16, A16, 16, 10, A16, None) == qr.QR_EINVAL
+    assert lib.qr_peak_mfma_codes(A16, 16, A16, 16, 10, None, None) == qr.QR_EINVAL
+    assert lib.qr_peak_mfma_codes(A16, 24, A16, 16, 10, A16, None) == qr.QR_ESHAPE
+    assert lib.qr_peak_mfma_codes(A16, 16, A16, 0, 10, A16, None) == qr.QR_ESHAPE
+    assert lib.qr_peak_mfma_codes(A16, 16, A16, 16, 0, A16, None) == qr.QR_ESHAPE
+    assert lib.qr_peak_mfma_codes(A16, 16, A16, 16, (1 << 24) + 1, A16, None) == qr.QR_ESHAPE
+    assert lib.qr_peak_mfma_codes(MIS, 16, A16, 16, 10, A16, None) == qr.QR_EALIGN
 
 
 def test_library_exports_every_declared_symbol():
