@@ -97,7 +97,8 @@ def parse():
     ap.add_argument("--trace-last", type=int, default=20, help="dispatches of the per-launch timing phase")
     ap.add_argument("--codes-sweep", action="store_true",
                     help="the config's int4 GEMM looped ~2 s each on constant, workload and uniformly random "
-                         "codes, with the shader clock sampled by rocm-smi meanwhile (one JSON line per kind)")
+                         "codes, then its rotate-quant on a constant and on the workload input, with the shader "
+                         "clock sampled by rocm-smi meanwhile (one JSON line per case)")
     return ap.parse_args()
 
 
@@ -528,6 +529,11 @@ def run_step(args):
         traffic = load_traffic(f"int4_gemm_{cfg.name}", "gemm_prefill_kernel", gemm_bytes)
         roofline = {"bound": "mfma", "kernel": "int4_gemm (gemm_prefill_kernel)", "achieved": round(gemm_tops, 2),
                     "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4)}
+        if peaks and "mfma_int8_codes_TOPS" in peaks:
+            # what the int8 MFMAs attain on this step's own codes (the clock under dense MFMA work falls as
+            # more operand bits toggle): the data-matched ceiling beside the datasheet one
+            roofline["peak_measured_on_codes"] = peaks["mfma_int8_codes_TOPS"]
+            roofline["frac_of_measured_on_codes"] = round(gemm_tops / peaks["mfma_int8_codes_TOPS"], 4)
     roofline["traffic"] = None if traffic is None else traffic["total_bytes"]
     roofline["traffic_detail"] = traffic
     roofline["achieved_from"] = "median of per-launch HIP event pairs on the launch stream"
@@ -587,9 +593,10 @@ def sclk_mhz():
 
 
 def codes_sweep(args):
-    """The same GEMM launch on three kinds of operand data.  The instruction
-    stream is identical; only the bits the MFMAs toggle differ, and with them
-    the clock this part sustains under the kernel."""
+    """The same GEMM launch on three kinds of operand data, then the same
+    rotate-quant launch on two inputs.  The instruction stream is identical;
+    only the bits the MFMAs toggle differ, and with them the clock this part
+    sustains under the kernel."""
     import threading
     import torch
     import workloads as W
@@ -616,8 +623,9 @@ def codes_sweep(args):
              ("workload", xc, wc),
              ("uniform", torch.randint(0, 256, xc.shape, dtype=torch.uint8, device=dev, generator=g),
               torch.randint(0, 256, wc.shape, dtype=torch.uint8, device=dev, generator=g))]
-    for name, a, w in kinds:
-        qr.int4_gemm(a, xs, w, ws, group, y=y)
+
+    def looped(name, fn, ops, what):
+        fn()
         torch.cuda.synchronize()
         clocks, stop = [], threading.Event()
 
@@ -633,7 +641,7 @@ def codes_sweep(args):
         e0.record()
         while time.perf_counter() - t0 < 2.0:
             for _ in range(10):
-                qr.int4_gemm(a, xs, w, ws, group, y=y)
+                fn()
             torch.cuda.synchronize()
             n += 10
         e1.record()
@@ -642,11 +650,21 @@ def codes_sweep(args):
         th.join()
         us = e0.elapsed_time(e1) * 1e3 / n
         late = clocks[len(clocks) // 3:]
-        print(json.dumps({"codes": name, "config": cfg.name, "launches": n, "us_per_launch": round(us, 1),
-                          "TOPS": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1),
+        print(json.dumps({"kernel": what, "data": name, "config": cfg.name, "launches": n,
+                          "us_per_launch": round(us, 1), **ops(us),
                           "sclk_MHz_median": statistics.median(late) if late else None,
                           "sclk_samples": len(clocks)}), flush=True)
         time.sleep(1.0)
+
+    for name, a, w in kinds:
+        looped(name, lambda: qr.int4_gemm(a, xs, w, ws, group, y=y),
+               lambda us: {"TOPS": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1)}, "int4_gemm")
+    # the rotate-quant kernel on the step's input and on a constant input
+    x = torch.from_numpy(W.make_x(cfg)).to(dev)
+    rq_bytes = M * K * 2 + M * K // 2 + M * (1 if group == 0 else K // group) * 4
+    for name, xx in (("constant", torch.full_like(x, 0.25)), ("workload", x)):
+        looped(name, lambda: qr.rotate_quant(xx, rot, group, xc, xs),
+               lambda us: {"GBs": round(rq_bytes / (us * 1e-6) / 1e9, 1)}, "rotate_quant")
 
 
 # ---------------------------------------------------------------- per-kernel suite
