@@ -67,9 +67,14 @@ constexpr int kMaxOff = 4 * kGroupPitch;
 constexpr int kSinkOff = kMaxOff + 16;
 constexpr int kAux = kSinkOff + 128 + 3 * kGroupPitch;
 
+// MC: the dense factor's order when fixed at compile time (the 11008-wide
+// input, m = 172: row offsets, code offsets and divisions by m / 2 become
+// immediates), 0 to take it from m_arg.
+template <int MC>
 __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron_kernel(
-    const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, int m, const float *__restrict__ dense,
+    const unsigned short *__restrict__ x, int64_t rows, int64_t ld_x, int m_arg, const float *__restrict__ dense,
     uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
+  const int m = MC > 0 ? MC : m_arg;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRowBufs * kRowBuf];   // X rows
   __shared__ __attribute__((aligned(16))) uint8_t aux[kAux];
   float *const wmax = (float *)(aux + kMaxOff);
@@ -331,8 +336,12 @@ hipError_t launch_rq_kron(const void *x, int64_t rows, int64_t ld_x, const RotAr
   const int cus = device_cu_count();
   const float scale_mul = (float)(1.0 / (7.0 * 8.0));   // 1/(7 sqrt(64))
   const int64_t grid = rows < 2 * cus ? rows : 2 * cus;   // two blocks per CU
-  rq_kron_kernel<<<dim3((unsigned)grid), dim3(64 * kWaves), 0, stream>>>(
-      (const unsigned short *)x, rows, ld_x, r.dense_m, r.dense, codes, scales, scale_mul);
+  if (r.dense_m == 172)
+    rq_kron_kernel<172><<<dim3((unsigned)grid), dim3(64 * kWaves), 0, stream>>>(
+        (const unsigned short *)x, rows, ld_x, r.dense_m, r.dense, codes, scales, scale_mul);
+  else
+    rq_kron_kernel<0><<<dim3((unsigned)grid), dim3(64 * kWaves), 0, stream>>>(
+        (const unsigned short *)x, rows, ld_x, r.dense_m, r.dense, codes, scales, scale_mul);
   return hipGetLastError();
 }
 
