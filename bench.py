@@ -63,6 +63,10 @@ STEP_CONFIGS = ("c3", "c2", "c4", "c5")
 # and c5, and costs ~2% at c3 (5.64 vs 5.75-5.78 ms per step in one process),
 # where each kernel fills the GPU by itself.
 DEFAULT_STREAMS = {"c3": 1, "c4": 1, "c2": 2, "c5": 2}
+# --graph 1 replays each step from a HIP graph captured per buffer set.  It
+# is off by default: the decode step took 55-57 us per step from graphs
+# against 35-38 us launched kernel by kernel (c2: no difference).
+DEFAULT_GRAPH = {"c3": 0, "c4": 0, "c2": 0, "c5": 0}
 # token rows of the CPU oracle sample per config (about 5-20 s on 16 cores)
 CPU_ROWS = {"c2": 2048, "c3": 2048, "c4": 512, "c5": 64}
 METRIC = "rotate+quant+int4 GEMM TOPS and GB/s at 7B/70B layer shapes; % of roofline"
@@ -75,6 +79,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c3", choices=STEP_CONFIGS)
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--graph", type=int, default=-1, choices=(-1, 0, 1),
+                    help="1: replay each step from a HIP graph captured per buffer set; 0: launch its kernels "
+                         "one by one; -1: the config's default")
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows in the CPU oracle sample (0 = default)")
     ap.add_argument("--streams", type=int, default=0,
                     help="HIP streams the steps alternate over (1: strictly one step after another; 0: the "
@@ -412,15 +419,41 @@ def run_step(args):
         src = s["y"][:, K:3 * K] if args.config == "c2" else s["kv"]
         qr.kv_quant(src, codes=s["kvc"], scales=s["kvs"], zeros=s["kvz"], stream=st)
 
+    use_graph = (args.graph if args.graph >= 0 else DEFAULT_GRAPH[cfg.name]) == 1
+    if use_graph:
+        # one graph per buffer set, captured after one eager pass (which sets
+        # up the library's per-process state); the step's kernels write only
+        # their outputs, so a replay recomputes the whole step
+        for s in sets:
+            rq(s)
+            gemm(s)
+            if has_kv:
+                kv(s)
+        torch.cuda.synchronize()
+        for s in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream()
+                rq(s, cs)
+                gemm(s, cs)
+                if has_kv:
+                    kv(s, cs)
+            s["graph"] = g
+        torch.cuda.synchronize()
+
     def step(i):
         s = sets[i % nsets]
         st = streams[i % len(streams)]
         if "done" in s and s["done_on"] is not st:
             st.wait_event(s["done"])   # the set's previous step, on another stream, has finished
-        rq(s, st)
-        gemm(s, st)
-        if has_kv:
-            kv(s, st)
+        if use_graph:
+            with torch.cuda.stream(st):
+                s["graph"].replay()
+        else:
+            rq(s, st)
+            gemm(s, st)
+            if has_kv:
+                kv(s, st)
         if len(streams) > 1:
             s["done"] = torch.cuda.Event()
             s["done"].record(st)
@@ -558,7 +591,7 @@ def run_step(args):
             "workload": f"{cfg.name}: {cfg.desc}; rotate {rot_desc} + {quant_desc} RTN, int4 GEMM (int8 MFMA, "
                         f"fp16 out)" + (f", 4-bit KV quant of {kv_T} tokens x {kv_H} K/V heads" if has_kv else ""),
             "M": M, "N": N, "K": K, "group": group, "codes": "int4", "mfma": "int8 -> int32",
-            "rotation": rot_desc, "buffer_sets": nsets, "streams": len(streams),
+            "rotation": rot_desc, "buffer_sets": nsets, "streams": len(streams), "graph": use_graph,
         },
         "kernels": kernels,
         "roofline": roofline,
