@@ -59,10 +59,12 @@ CACHE_BYTES = 1 << 30        # cycle buffers over >= 1 GiB (MALL is 256 MB)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 STEP_CONFIGS = ("c3", "c2", "c4", "c5")
 # Steps alternate over this many HIP streams unless --streams says otherwise:
-# overlapping consecutive steps helps the short latency-bound launches of c2
-# and c5, and costs ~2% at c3 (5.64 vs 5.75-5.78 ms per step in one process),
-# where each kernel fills the GPU by itself.
-DEFAULT_STREAMS = {"c3": 1, "c4": 1, "c2": 2, "c5": 2}
+# overlapping consecutive steps helps c2's short launches (104 vs 108-109 us
+# per step), costs ~2% at c3 (5.64 vs 5.75-5.78 ms), where each kernel fills
+# the GPU by itself, and costs c5 15-20% (21.3 vs 25.2-26.6 us): the decode
+# step is bound by the host's ~7 us per launch call, and the second stream
+# adds event bookkeeping on the host every step.
+DEFAULT_STREAMS = {"c3": 1, "c4": 1, "c2": 2, "c5": 1}
 # --graph 1 replays each step from a HIP graph captured per buffer set.  It
 # is off by default: the decode step took 55-57 us per step from graphs
 # against 35-38 us launched kernel by kernel (c2: no difference).
