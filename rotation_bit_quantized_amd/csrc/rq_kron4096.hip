@@ -66,8 +66,11 @@ __device__ __forceinline__ unsigned swiglu2(unsigned gw, unsigned uw) {
   return __builtin_bit_cast(unsigned, r);
 }
 
+// Two blocks per CU, except at M = 8, whose wave needs more than the 256
+// registers that two waves per SIMD leave it (one block per CU; the launch
+// sizes its grid from the occupancy query).
 template <int M, bool FUSED>
-__global__ __launch_bounds__(64 * kWaves, 2) void rq_kron4096_kernel(
+__global__ __launch_bounds__(64 * kWaves, M == 8 ? 1 : 2) void rq_kron4096_kernel(
     const unsigned short *__restrict__ x, const unsigned short *__restrict__ up, int64_t rows, int64_t ld_x,
     const float *__restrict__ dense, uint8_t *__restrict__ codes, float *__restrict__ scales, float scale_mul) {
   static_assert(M >= 2 && M <= 8, "dense factor size");
