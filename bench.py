@@ -33,7 +33,7 @@ bounded row sample of the same workload and extrapolated to the whole step;
 `peaks_measured` holds what this GPU attains for a streaming copy and for
 back-to-back int8 / fp16 MFMAs (include/qr_peaks.h), the second denominators.
 
-  python bench.py [--config c3] [--steps 20] [--warmup 5] [--streams N] [--no-cpu]
+  python bench.py [--config c3] [--steps K] [--warmup W] [--streams N] [--graph 0|1] [--no-cpu]
   python bench.py --suite [--only case,...]      # every kernel at every shape
 """
 from __future__ import annotations
@@ -65,6 +65,11 @@ STEP_CONFIGS = ("c3", "c2", "c4", "c5")
 # step is bound by the host's ~7 us per launch call, and the second stream
 # adds event bookkeeping on the host every step.
 DEFAULT_STREAMS = {"c3": 1, "c4": 1, "c2": 2, "c5": 1}
+# Timed and warm-up steps by default: the short steps of c2 (~0.1 ms) and c5
+# (~20 us) need many more of them than c3 and c4 (~5 ms) for a timed region
+# that a pair of events measures well (20 decode steps gave 35.8 us per step
+# where 200 gave 21.3).
+DEFAULT_STEPS = {"c3": (20, 5), "c4": (20, 5), "c2": (200, 20), "c5": (500, 50)}
 # --graph 1 replays each step from a HIP graph captured per buffer set.  It
 # is off by default: the decode step took 55-57 us per step from graphs
 # against 35-38 us launched kernel by kernel (c2: no difference).
@@ -77,8 +82,8 @@ METRIC = "rotate+quant+int4 GEMM TOPS and GB/s at 7B/70B layer shapes; % of roof
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (0: the config's default)")
+    ap.add_argument("--warmup", type=int, default=-1, help="untimed steps first (-1: the config's default)")
     ap.add_argument("--config", default="c3", choices=STEP_CONFIGS)
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--graph", type=int, default=-1, choices=(-1, 0, 1),
@@ -363,6 +368,10 @@ def run_step(args):
     cfg = W.CONFIGS[args.config]
     M, N, K, group = cfg.M, cfg.N, cfg.K, cfg.group
     G = 1 if group == 0 else K // group
+    if args.steps <= 0:
+        args.steps = DEFAULT_STEPS[cfg.name][0]
+    if args.warmup < 0:
+        args.warmup = DEFAULT_STEPS[cfg.name][1]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
