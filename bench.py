@@ -74,8 +74,10 @@ DEFAULT_STEPS = {"c3": (20, 5), "c4": (20, 5), "c2": (200, 20), "c5": (500, 50)}
 # is off by default: the decode step took 55-57 us per step from graphs
 # against 35-38 us launched kernel by kernel (c2: no difference).
 DEFAULT_GRAPH = {"c3": 0, "c4": 0, "c2": 0, "c5": 0}
-# token rows of the CPU oracle sample per config (about 5-20 s on 16 cores)
+# token rows of the CPU oracle sample per config (one pass takes ~0.05-7 s on
+# 16 cores); passes repeat until CPU_MIN_SECONDS of oracle work are timed
 CPU_ROWS = {"c2": 2048, "c3": 2048, "c4": 512, "c5": 64}
+CPU_MIN_SECONDS = 10.0
 METRIC = "rotate+quant+int4 GEMM TOPS and GB/s at 7B/70B layer shapes; % of roofline"
 
 
@@ -225,9 +227,11 @@ def oracle_rows_rotated(x, cfg, signs, dense):
 def cpu_baseline(cfg, rows, kv_rows):
     """The oracle on a bounded sample: `rows` token rows through rotate,
     quantize, int64 GEMM against all N output channels and fp64 dequantize,
-    plus the KV quantizer on those rows' K and V (c2, c5).  Weight preparation
-    (offline in the method) is not timed.  Throughput is extrapolated
-    linearly to the whole step (every stage is per token)."""
+    plus the KV quantizer on those rows' K and V (c2, c5).  The pass is
+    repeated, each time from the input, until at least CPU_MIN_SECONDS of
+    work have been timed.  Weight preparation (offline in the method) is not
+    timed.  Throughput is extrapolated linearly to the whole step (every
+    stage is per token)."""
     import oracle as O
     import workloads as W
     threads = len(os.sched_getaffinity(0))
@@ -236,22 +240,27 @@ def cpu_baseline(cfg, rows, kv_rows):
     signs, dense = W.make_signs(cfg), W.make_dense(cfg)
     wr = oracle_rows_rotated(np.ascontiguousarray(w.T), cfg, signs, dense).T      # R^T W
     qw, sw = O.quantize_weights(wr, cfg.group)
-    t0 = time.perf_counter()
-    y = oracle_rows_rotated(x, cfg, signs, dense)
-    qx, sx, _ = O.quantize_symmetric(y, cfg.group)
     blocks = np.array_split(np.arange(cfg.N), threads)
-    with cf.ThreadPoolExecutor(threads) as ex:
-        parts = list(ex.map(lambda b: O.int_gemm(qx, qw[b], cfg.group), blocks))
-    acc = np.concatenate(parts, axis=-1)
-    out = O.dequantize_output(acc, sx, sw, cfg.group)
-    if kv_rows is not None:
-        for t in kv_rows(out):
-            O.kv_quantize(t)
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        y = oracle_rows_rotated(x, cfg, signs, dense)
+        qx, sx, _ = O.quantize_symmetric(y, cfg.group)
+        with cf.ThreadPoolExecutor(threads) as ex:
+            parts = list(ex.map(lambda b: O.int_gemm(qx, qw[b], cfg.group), blocks))
+        acc = np.concatenate(parts, axis=-1)
+        out = O.dequantize_output(acc, sx, sw, cfg.group)
+        if kv_rows is not None:
+            for t in kv_rows(out):
+                O.kv_quantize(t)
+        passes += 1
+        if time.perf_counter() - t0 >= CPU_MIN_SECONDS:
+            break
     dt = time.perf_counter() - t0
-    ops = 2.0 * rows * cfg.N * cfg.K
+    ops = 2.0 * rows * cfg.N * cfg.K * passes
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"{rows} of {cfg.M} token rows (rate extrapolated linearly to the whole step): fp64 "
+            "seconds": round(dt, 3), "passes": passes,
+            "sample": f"{rows} of {cfg.M} token rows, {passes} timed passes (rate extrapolated linearly to the whole step): fp64 "
                       f"rotation ({'rotate_kron' if cfg.dense_m > 1 else 'fwht'}), RTN, int64 GEMM against all "
                       f"{cfg.N} channels (column blocks over {threads} threads), fp64 dequant"
                       + (", KV quant of the sampled rows' K and V" if kv_rows is not None else "")
