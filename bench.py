@@ -94,8 +94,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows in the CPU oracle sample (0 = default)")
     ap.add_argument("--streams", type=int, default=0,
                     help="HIP streams the steps alternate over (1: strictly one step after another; 0: the "
-                         "workload's default, 2 for the short c2 and c5 steps whose latency-bound launches "
-                         "gain from overlapping, 1 for c3 and c4 whose kernels each fill the GPU)")
+                         "workload's default, 2 for the short c2 step whose launches gain from overlapping, "
+                         "1 for c3 and c4 whose kernels each fill the GPU and for c5 whose step is bound "
+                         "by the host's launch calls)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run one probe copy of this many MiB (HBM counter calibration)")
