@@ -423,6 +423,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   // The DMA of K-tile kt+2 goes into this tile's buffer, free after the
   // chunk-2 barrier: half of it interleaved with the MFMAs of chunk 2, half
   // with those of chunk 3; it is waited for at chunk 2 of tile kt+1.
+  // Wave priority falls chunk by chunk from the barrier on (3 for chunk 2,
+  // then 2, 1, 0): the two waves of a SIMD share its issue slots, and the
+  // older one wins every tie, so without this it finished each barrier
+  // interval well ahead and idled at the barrier while the younger ran
+  // alone (~1650 against ~300 cycles of wait per K-tile at 256 x 192).  A
+  // wave that is a chunk ahead now yields to the one behind it.
   constexpr int kNext = 0, kNextNoDma = 1, kLastFull = 2, kLastShort = 3;
   constexpr int Q1 = LOADS / 2;
   static_assert(STAGES == 2, "the refill schedule assumes two stages");
@@ -451,11 +457,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
     } else {
       // chunk 0
       chunk_fence();
+      __builtin_amdgcn_s_setprio(1);
       read_raw(st, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
       compute(0, 1, start0, std::true_type{}, NoDma{}, 0, 0);
       // chunk 1
       chunk_fence();
+      __builtin_amdgcn_s_setprio(0);
       read_raw(st, 3, 1);
       __builtin_amdgcn_sched_barrier(0);
       compute(1, 0, false, std::true_type{}, NoDma{}, 0, 0);
@@ -473,6 +481,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
         __builtin_amdgcn_s_barrier();
         read_raw(nst, 0, 0);
       }
+      __builtin_amdgcn_s_setprio(3);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (mode == kNext)
         compute(0, 1, start1, std::true_type{}, DmaRange<0, Q1>{}, dkt, dstage);
@@ -481,6 +490,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
       // chunk 3
       if constexpr (NEXT) {
         chunk_fence();
+        __builtin_amdgcn_s_setprio(2);
         read_raw(nst, 1, 1);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (mode == kNext)
