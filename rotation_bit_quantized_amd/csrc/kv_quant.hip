@@ -106,7 +106,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void kv_quant_kernel(
   if (wave_id < ntiles) load_tile(wave_id, raw);
   if (wave_id + wave_stride < ntiles) load_tile(wave_id + wave_stride, nxt);
 
-  for (int64_t tile = wave_id; tile < ntiles; tile += wave_stride) {
+  int it = 0;
+  for (int64_t tile = wave_id; tile < ntiles; tile += wave_stride, ++it) {
+    set_prio_by_progress(it);   // the waves sharing a SIMD keep pace
     v4u nxt2[4];
     if (tile + 2 * wave_stride < ntiles) load_tile(tile + 2 * wave_stride, nxt2);
 

@@ -79,6 +79,21 @@ __device__ __forceinline__ void wait_vm() {
 // s_waitcnt lgkmcnt(0), vmcnt and expcnt left alone.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Wave priority 3, 2, 1, 0 for iterations k = 0, 1, 2, 3 (mod 4) of a
+// persistent loop over rows or tiles (k wave-uniform).  Where waves of equal
+// work share a SIMD, the hardware gives every issue tie to the older wave,
+// so it finishes its share well ahead and the younger one then runs its last
+// iterations alone; with the priority falling as a wave advances, the one
+// that is ahead yields to the one behind and both finish together.
+__device__ __forceinline__ void set_prio_by_progress(int k) {
+  switch (k & 3) {
+    case 0: __builtin_amdgcn_s_setprio(3); break;
+    case 1: __builtin_amdgcn_s_setprio(2); break;
+    case 2: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
 // 2 x 2 transposes of (register, lane bit 4) and (register, lane bit 5).
 __device__ __forceinline__ void swap16(float &a, float &b) {
   auto r = __builtin_amdgcn_permlane16_swap(f2u(a), f2u(b), false, false);

@@ -180,6 +180,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void rq_kron_kernel(
   float prev_mx = 0.f;
   int xb = 0, db = 2;
   for (int k = 0; k < nblk; ++k) {
+    // the two blocks of a CU keep pace (two blocks per CU: the older one
+    // otherwise finished ~19% of the launch ahead, the younger then alone)
+    set_prio_by_progress(k);
     // Row r_k has landed.  Issued after its DMA (in step k - 2): the DMA of
     // r_{k+1} (kKS operations, in step k - 1) and, for k >= 2, the two code
     // stores of r_{k-2} per wave before it (the scale store of wave 0 only

@@ -149,7 +149,8 @@ __global__ __launch_bounds__(64 * kWaves, M == 8 ? 1 : 2) void rq_kron4096_kerne
   issue_row(row);
   bool first = true;
   constexpr int kPieces = FUSED ? kRowBytes / 16 / (64 * kWaves) : 1;   // 16-byte pieces of up per thread
-  for (; row < rows; row += stride) {
+  for (int k = 0; row < rows; row += stride, ++k) {
+    set_prio_by_progress(k);   // the two blocks of a CU keep pace
     // FUSED: this row's up pieces, loaded while the gate row's DMA finishes
     v4u uv[kPieces];
     if constexpr (FUSED) {

@@ -213,6 +213,7 @@ __global__ __launch_bounds__(64 * waves_of<L>()) void rq_pow2_kernel(
 
   int it = 0;
   for (int64_t row = wave_id; row < rows; row += wave_stride, ++it) {
+    set_prio_by_progress(it);   // the waves sharing a SIMD keep pace
     const uint8_t *buf = bufs + (kBufs == 2 ? (it & 1) * ROWB : 0);
     // Wait for this row's DMA.  Two buffers: issued after it are the DMA of
     // the wave's following row (when that row exists; DMAs of rows past the
