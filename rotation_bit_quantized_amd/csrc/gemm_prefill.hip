@@ -421,8 +421,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   // by another; kLastFull: the last tile, 256 codes; kLastShort: the last
   // tile, 128 codes.
   // The DMA of K-tile kt+2 goes into this tile's buffer, free after the
-  // chunk-2 barrier: half of it interleaved with the MFMAs of chunk 2, half
-  // with those of chunk 3; it is waited for at chunk 2 of tile kt+1.
+  // chunk-2 barrier: about a third of it interleaved with the MFMAs of chunk
+  // 2, the rest with those of chunk 3; it is waited for at chunk 2 of tile
+  // kt+1.  Chunk 2 follows the barrier, where the waves of a SIMD are closest
+  // together and compete hardest for issue slots: with half of the DMA there
+  // the launch took 1-3% longer.
   // Wave priority falls chunk by chunk from the barrier on (3 for chunk 2,
   // then 2, 1, 0): the two waves of a SIMD share its issue slots, and the
   // older one wins every tie, so without this it finished each barrier
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, OCC * 4 / (WAVES_M * WAVES_
   // alone (~1650 against ~300 cycles of wait per K-tile at 256 x 192).  A
   // wave that is a chunk ahead now yields to the one behind it.
   constexpr int kNext = 0, kNextNoDma = 1, kLastFull = 2, kLastShort = 3;
-  constexpr int Q1 = LOADS / 2;
+  constexpr int Q1 = LOADS / 3 > LOADS - KS * FM * FN ? LOADS / 3 : LOADS - KS * FM * FN;
   static_assert(STAGES == 2, "the refill schedule assumes two stages");
   static_assert(Q1 <= KS * FM * FN && LOADS - Q1 <= KS * FM * FN, "one DMA instruction per MFMA at most");
   auto tile = [&](int kt, auto mode_c) __attribute__((always_inline)) {
